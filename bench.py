@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark: one MLA decode step (absorb_q -> append_cache -> decode -> out_proj)
+on synthetic DeepSeek-V3-shaped inputs on one MI355X.
+
+Prints ONE JSON line on stdout.  ``value`` = cached-token reads per second over
+the whole step (one read = one 576-value latent row consumed by all 128 heads of
+one query token), inputs resident in HBM.  The ``roofline`` object covers the
+decode call (the dominant kernel) with its algorithmic bytes, timed live with
+HIP events on the library's stream; ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload batch64]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode: cached-token reads/s, % of HBM & bf16 MFMA roofline (V3 shapes)"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "head_latent_attention_05_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def kv_reads(inp) -> int:
+    """Sum over query tokens of the rows each attends."""
+    tot = 0
+    for b in range(len(inp.kv_lens)):
+        L, q = int(inp.kv_lens[b]), int(inp.q_lens[b])
+        if inp.workload.causal:
+            tot += sum(L - q + j + 1 for j in range(q))
+        else:
+            tot += q * L
+    return tot
+
+
+def traffic_from_counters(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    try:
+        c = json.load(open(COUNTERS))
+        e = c.get(workload)
+        if not e or e.get("source_sha") != source_hash():
+            return None
+        return e["traffic_bytes"]
+    except Exception:
+        return None
+
+
+def cpu_baseline(workload: str, budget_s: float):
+    """The oracle (append + naive explicit-decompression attention, fp64, all
+    heads) on the first sequences of the workload, until ~budget_s of CPU work."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from head_latent_attention_05_amd import synth
+    from oracle import mla_oracle as O
+
+    full = synth.make_inputs(workload)
+    wl = full.workload
+    lens = [int(x) for x in full.kv_lens]
+    done_tokens, spent, nseq = 0, 0.0, 0
+    for b, L in enumerate(lens):
+        inp = synth.make_inputs(wl, kv_lens=[L], seed=1000 + b)
+        t0 = time.perf_counter()
+        O.step(inp)
+        spent += time.perf_counter() - t0
+        done_tokens += kv_reads(inp)
+        nseq += 1
+        if spent >= budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": done_tokens / spent, "unit": "cached-token reads/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{nseq} of {len(lens)} sequences of '{workload}' (kv_len {lens[:nseq]}), "
+                      f"all heads, append + naive fp64 attention, {spent:.1f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="batch64")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pool-copies", type=int, default=0,
+                    help="cache copies rotated between steps (0: enough for >= 1 GB)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(decode shards by sequence with no exchange; see DESIGN.md).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from head_latent_attention_05_amd import synth
+    from head_latent_attention_05_amd.step import DeviceStep
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    inp = synth.make_inputs(args.workload)
+    d = inp.dims
+    reads = kv_reads(inp)
+    pool_bytes = inp.num_blocks * 64 * d.row * (2 if d.dtype == "bf16" else 4)
+    copies = args.pool_copies or max(1, min(8, -(-(1 << 30) // pool_bytes)))
+    log(f"[bench] workload={args.workload} T={inp.T} kv_reads={reads} pool={pool_bytes/1e6:.1f} MB "
+        f"x{copies}")
+    st = DeviceStep(inp, pool_copies=copies)
+    pools = st.pools
+
+    def step(i, ev=None):
+        p = pools[i % copies]
+        st.absorb()
+        st.append(p)
+        if ev is not None:
+            ev[0].record()
+        st.decode(p)
+        if ev is not None:
+            ev[1].record()
+        st.project()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg = float(np.mean(dec_ms))
+    log(f"[bench] step {ms*1e3:.1f} us (wall {wall/args.steps*1e6:.1f} us), decode avg "
+        f"{dec_avg*1e3:.1f} us, p10 {np.percentile(dec_ms,10)*1e3:.1f} p90 "
+        f"{np.percentile(dec_ms,90)*1e3:.1f}")
+    assert int(st.dev_error.item()) == 0
+
+    esz = 2 if d.dtype == "bf16" else 4
+    dec_bytes = reads * d.row * esz + inp.T * d.num_heads * (d.row + d.d_latent) * esz
+    dec_flops = reads * 2 * d.num_heads * (d.row + d.d_latent)
+    achieved_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
+    achieved_tfs = dec_flops / (dec_avg * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": reads / (ms * 1e-3),
+        "unit": "cached-token reads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if d.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": int(len(inp.kv_lens)),
+                   "query_tokens": inp.T, "kv_reads_per_step": reads,
+                   "kv_len_min": int(inp.kv_lens.min()), "kv_len_max": int(inp.kv_lens.max()),
+                   "heads": d.num_heads, "d_latent": d.d_latent, "d_rope": d.d_rope,
+                   "block_size": 64, "causal": bool(inp.workload.causal),
+                   "cache_copies_rotated": copies},
+        "roofline": {"kernel": "mla_decode", "bound": "hbm", "achieved": achieved_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic_from_counters(args.workload),
+                     "algorithmic_bytes": dec_bytes, "avg_launch_us": dec_avg * 1e3,
+                     "mfma": {"achieved": achieved_tfs, "peak": MFMA_BF16_PEAK_TFS,
+                              "unit": "TFLOP/s", "frac": achieved_tfs / MFMA_BF16_PEAK_TFS,
+                              "algorithmic_flops": dec_flops}},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        rec["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

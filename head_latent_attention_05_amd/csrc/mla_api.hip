@@ -1,0 +1,267 @@
+// libmla C ABI: argument checks, split planning and kernel launches.
+// The public contract (math, layouts, errors) is documented in include/mla.h.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "mla_internal.h"
+
+namespace mla {
+hipError_t launch_absorb_generic(const mla_config& c, int T, const void* q_nope,
+                                 const void* w_uk, void* q_lat, hipStream_t st);
+hipError_t launch_out_proj_generic(const mla_config& c, int T, const void* o_lat,
+                                   const void* w_uv, float* out, hipStream_t st);
+bool v3_kernels_available();
+
+namespace {
+
+bool is_v3_bf16(const mla_config& c) {
+  return c.dtype == MLA_BF16 && c.num_heads == 128 && c.d_latent == 512 && c.d_rope == 64 &&
+         c.d_nope == 128 && c.d_v == 128 && c.block_size == 64;
+}
+
+bool is_f32_supported(const mla_config& c) {
+  const bool dc_ok = c.d_latent == 64 || c.d_latent == 128 || c.d_latent == 256 ||
+                     c.d_latent == 512;
+  const bool dr_ok = c.d_rope == 16 || c.d_rope == 32 || c.d_rope == 64;
+  return c.dtype == MLA_F32 && c.num_heads >= 1 && c.num_heads <= 128 && dc_ok && dr_ok &&
+         c.d_nope >= 1 && c.d_nope <= 256 && c.d_v >= 1 && c.d_v <= 256 && c.block_size == 64;
+}
+
+mla_status check_cfg(const mla_config* c) {
+  if (!c) return MLA_ERR_INVALID_ARG;
+  if (c->num_heads < 1 || c->d_latent < 1 || c->d_rope < 2 || (c->d_rope & 1) ||
+      c->d_nope < 1 || c->d_v < 1 || c->block_size < 1 || !(c->softmax_scale > 0.f) ||
+      !isfinite(c->softmax_scale))
+    return MLA_ERR_INVALID_ARG;
+  if (c->dtype != MLA_F32 && c->dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+  if (!is_v3_bf16(*c) && !is_f32_supported(*c)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elt(const mla_config& c) { return c.dtype == MLA_BF16 ? 2 : 4; }
+
+mla_status from_hip(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// Compute units of the current device (cached per device id).
+mla_status device_cus(int* out) {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  std::lock_guard<std::mutex> g(mu);
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return MLA_OK;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return MLA_ERR_HIP;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  *out = n;
+  return MLA_OK;
+}
+
+struct HostPlan {
+  int32_t T = 0;
+  int64_t U = 0;
+  int32_t G = 0;
+  size_t ws_bytes = 0;
+  size_t lse_bytes = 0;
+};
+
+mla_status plan_decode(const mla_config& c, int32_t B, const int32_t* qs, const int32_t* kl,
+                       int32_t causal, int32_t num_wg, HostPlan* hp) {
+  if (B < 1 || !qs || !kl || num_wg < 0) return MLA_ERR_INVALID_ARG;
+  if (qs[0] != 0) return MLA_ERR_INVALID_ARG;
+  int64_t U = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t q = (int64_t)qs[b + 1] - qs[b];
+    const int64_t L = kl[b];
+    if (q < 0 || L < 1 || q > L) return MLA_ERR_INVALID_ARG;
+    U += seq_units_before(L, q, q, c.block_size, causal ? 1 : 0);
+  }
+  hp->T = qs[B];
+  hp->U = U;
+  if (U == 0) {
+    hp->G = 0;
+    hp->ws_bytes = 0;
+    return MLA_OK;
+  }
+  int64_t G = num_wg;
+  if (G == 0) {
+    int cus = 0;
+    mla_status s = device_cus(&cus);
+    if (s != MLA_OK) return s;
+    G = cus;
+  }
+  if (G > U) G = U;
+  if (G > (1 << 30)) G = 1 << 30;
+  hp->G = (int32_t)G;
+  if (G == 1) {
+    hp->ws_bytes = 0;
+    hp->lse_bytes = 0;
+  } else {
+    hp->lse_bytes = ws_align(ws_lse_bytes(G, c.num_heads));
+    hp->ws_bytes = hp->lse_bytes + (size_t)(2 * G) * c.num_heads * c.d_latent * elt(c);
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported dims/dtype";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+mla_status mla_rope_table(float* cos_host, float* sin_host, int32_t max_pos, int32_t d_rope,
+                          double theta) {
+  if (!cos_host || !sin_host || max_pos < 1 || d_rope < 2 || (d_rope & 1) || !(theta > 0))
+    return MLA_ERR_INVALID_ARG;
+  const int half = d_rope / 2;
+  for (int i = 0; i < half; ++i) {
+    const double inv = 1.0 / pow(theta, 2.0 * i / (double)d_rope);
+    for (int64_t p = 0; p < max_pos; ++p) {
+      const double a = (double)p * inv;
+      cos_host[p * half + i] = (float)cos(a);
+      sin_host[p * half + i] = (float)sin(a);
+    }
+  }
+  return MLA_OK;
+}
+
+mla_status mla_absorb_q(const mla_config* cfg, int32_t T, const void* q_nope, const void* w_uk,
+                        void* q_lat, void* stream) {
+  mla_status s = check_cfg(cfg);
+  if (s != MLA_OK) return s;
+  if (T < 0) return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!q_nope || !w_uk || !q_lat) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_lat)) return MLA_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (is_v3_bf16(*cfg) && v3_kernels_available()) return from_hip(launch_absorb_q(*cfg, T, q_nope, w_uk, q_lat, st));
+  return from_hip(launch_absorb_generic(*cfg, T, q_nope, w_uk, q_lat, st));
+}
+
+mla_status mla_append_cache(const mla_config* cfg, int32_t T, const void* c_kv, const void* k_pe,
+                            const void* q_pe, const int32_t* token_seq, const int32_t* positions,
+                            const int32_t* block_table, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int64_t num_pool_blocks,
+                            const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                            void* kv_pool, void* q_lat, uint32_t* dev_error, void* stream) {
+  mla_status s = check_cfg(cfg);
+  if (s != MLA_OK) return s;
+  if (T < 0) return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!c_kv || !k_pe || !token_seq || !positions || !block_table || !rope_cos || !rope_sin ||
+      !kv_pool)
+    return MLA_ERR_INVALID_ARG;
+  if ((q_pe == nullptr) != (q_lat == nullptr)) return MLA_ERR_INVALID_ARG;
+  if (num_seqs < 1 || max_blocks_per_seq < 1 || num_pool_blocks < 1 || max_pos < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned16(c_kv) || !aligned16(k_pe) || !aligned16(kv_pool) ||
+      (q_pe && (!aligned16(q_pe) || !aligned16(q_lat))))
+    return MLA_ERR_INVALID_ARG;
+  return from_hip(launch_append(*cfg, T, c_kv, k_pe, q_pe, token_seq, positions, block_table,
+                                num_seqs, max_blocks_per_seq, num_pool_blocks, rope_cos,
+                                rope_sin, max_pos, kv_pool, q_lat, dev_error,
+                                (hipStream_t)stream));
+}
+
+mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t num_seqs,
+                                     const int32_t* q_start_host, const int32_t* kv_lens_host,
+                                     int32_t causal, int32_t num_workgroups, size_t* bytes) {
+  mla_status s = check_cfg(cfg);
+  if (s != MLA_OK) return s;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  HostPlan hp;
+  s = plan_decode(*cfg, num_seqs, q_start_host, kv_lens_host, causal, num_workgroups, &hp);
+  if (s != MLA_OK) return s;
+  *bytes = hp.ws_bytes;
+  return MLA_OK;
+}
+
+mla_status mla_decode(const mla_config* cfg, int32_t num_seqs, const int32_t* q_start,
+                      const int32_t* kv_lens, const int32_t* q_start_host,
+                      const int32_t* kv_lens_host, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, int64_t num_pool_blocks, const void* q_lat,
+                      const void* kv_pool, int32_t causal, int32_t num_workgroups,
+                      void* workspace, size_t workspace_bytes, void* o_lat, uint32_t* dev_error,
+                      void* stream) {
+  mla_status s = check_cfg(cfg);
+  if (s != MLA_OK) return s;
+  HostPlan hp;
+  s = plan_decode(*cfg, num_seqs, q_start_host, kv_lens_host, causal, num_workgroups, &hp);
+  if (s != MLA_OK) return s;
+  if (hp.T == 0) return MLA_OK;
+  if (!q_start || !kv_lens || !block_table || !q_lat || !kv_pool || !o_lat)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_lat) || !aligned16(kv_pool) || !aligned16(o_lat)) return MLA_ERR_INVALID_ARG;
+  if (num_pool_blocks < 1) return MLA_ERR_INVALID_ARG;
+  int64_t maxL = 0;
+  for (int b = 0; b < num_seqs; ++b) maxL = kv_lens_host[b] > maxL ? kv_lens_host[b] : maxL;
+  if (max_blocks_per_seq < (maxL + cfg->block_size - 1) / cfg->block_size)
+    return MLA_ERR_INVALID_ARG;
+  if (hp.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < hp.ws_bytes || !aligned16(workspace))
+      return MLA_ERR_WORKSPACE;
+  }
+  DecodeArgs a;
+  a.plan.q_start = q_start;
+  a.plan.kv_lens = kv_lens;
+  a.plan.B = num_seqs;
+  a.plan.T = hp.T;
+  a.plan.block_size = cfg->block_size;
+  a.plan.causal = causal ? 1 : 0;
+  a.plan.G = hp.G;
+  a.plan.U = hp.U;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_pool_blocks;
+  a.q_lat = q_lat;
+  a.pool = kv_pool;
+  a.o_lat = o_lat;
+  a.ws_lse = (float*)workspace;
+  a.ws_o = workspace ? (void*)((char*)workspace + hp.lse_bytes) : nullptr;
+  a.err = dev_error;
+  a.scale_log2 = cfg->softmax_scale * kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (is_v3_bf16(*cfg) && v3_kernels_available())
+    e = launch_decode_v3(a, st);
+  else
+    e = launch_decode_generic(*cfg, a, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (hp.G > 1) e = launch_merge(*cfg, a, st);
+  return from_hip(e);
+}
+
+mla_status mla_out_proj(const mla_config* cfg, int32_t T, const void* o_lat, const void* w_uv,
+                        float* out, void* stream) {
+  mla_status s = check_cfg(cfg);
+  if (s != MLA_OK) return s;
+  if (T < 0) return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (is_v3_bf16(*cfg) && v3_kernels_available()) return from_hip(launch_out_proj(*cfg, T, o_lat, w_uv, out, st));
+  return from_hip(launch_out_proj_generic(*cfg, T, o_lat, w_uv, out, st));
+}
+
+}  // extern "C"

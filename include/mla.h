@@ -1,0 +1,187 @@
+/*
+ * libmla -- Multi-Head Latent Attention (MLA) decode with weight absorption on
+ * AMD Instinct MI355X (gfx950).  Plain C ABI: host or device pointers and sizes,
+ * no framework types.
+ *
+ * What the library computes (sources are web pages, cited by page and section):
+ *
+ *   [MLA explainer]    xxmr.cn/news/206254, sections "MLA的计算过程" (stage 2A:
+ *                      explicit decompression; stage 2B: absorbed inference) and
+ *                      "MLA的实现" (RoPE module, forward_inference_absorbed).
+ *   [MLA architecture] intelliparadigm.com, "MLA架构：低秩注意力机制优化LLM显存与计算效率",
+ *                      section 1 (128 heads; qk head = 128 no-RoPE + 64 RoPE;
+ *                      576 cached values per token), 3.1 (absorption),
+ *                      3.2 (latent cache + shared RoPE key cache), 4.2 (pre-allocated
+ *                      cache; RoPE fused with the cache update).
+ *   [MLA deep dive]    mlqm.cn/news/500296, 2.3 (weight absorption), 5.1 (paged cache).
+ *
+ * One decode/prefill step for a batch of sequences is four calls on one stream:
+ *
+ *   mla_absorb_q      q_lat[:, :, 0:d_c]  = W_UK^T q_nope            (per head)
+ *   mla_append_cache  pool rows <- [c_kv | RoPE(k_pe)];  q_lat[:, :, d_c:] = RoPE(q_pe)
+ *   mla_decode        o_lat = softmax(scale * q_lat . rows^T) . c_kv  (paged, split-KV)
+ *   mla_out_proj      out = W_UV o_lat                                 (per head)
+ *
+ * Full per-head K and V are never formed.  The result equals explicit-decompression
+ * attention with scale 1/sqrt(d_nope + d_rope) up to rounding ([MLA architecture]
+ * 3.1: absorption is associativity of the matrix products).
+ *
+ * Supported shapes (anything else returns MLA_ERR_UNSUPPORTED):
+ *   bf16: num_heads=128, d_latent=512, d_rope=64, d_nope=128, d_v=128, block_size=64
+ *         (DeepSeek-V3 shapes; bf16 storage, fp32 accumulation)
+ *   f32 : num_heads in [1, 128], d_latent in {64, 128, 256, 512}, d_rope in {16, 32, 64},
+ *         d_nope, d_v in [1, 256], block_size=64 (all-fp32 test mode)
+ *
+ * Layouts: row-major, last index contiguous.  T = number of query (new) tokens.
+ *   q_nope [T][H][d_nope]      q_pe  [T][H][d_rope]     q_lat [T][H][d_latent + d_rope]
+ *   c_kv   [T][d_latent]       k_pe  [T][d_rope]
+ *   w_uk   [H][d_nope][d_latent]     w_uv [H][d_v][d_latent]
+ *   kv_pool [num_blocks][block_size][d_latent + d_rope]   row = [c_kv | RoPE(k_pe)]
+ *   o_lat  [T][H][d_latent]    out   [T][H][d_v]  (always fp32)
+ *   block_table [num_seqs][max_blocks_per_seq] int32, physical block ids, -1 = unused
+ * Element type of every "void*" tensor is the config dtype (bf16 or fp32).
+ * Device tensors must be 16-byte aligned.
+ *
+ * Ownership and execution: every buffer is owned by the caller.  The library never
+ * allocates device memory and keeps no device state.  Calls enqueue kernels on the
+ * given stream (a hipStream_t; NULL = the default stream), return without waiting,
+ * and never synchronise the device.  Calls are reentrant.
+ *
+ * Errors: a call validates everything it can see on the host and returns a status
+ * without launching anything when a check fails.  Device-resident indices
+ * (positions, sequence ids, block ids) are checked inside the kernels: an entry that
+ * is out of range is skipped (nothing is written for it) and, if the caller passes
+ * an error word, bit flags are OR-ed into it (see MLA_DEVERR_*).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer, bad length */
+  MLA_ERR_UNSUPPORTED = 2, /* dims / dtype combination not built */
+  MLA_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  MLA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Bits OR-ed into the optional device error word by the kernels. */
+#define MLA_DEVERR_POSITION 1u /* position < 0 or >= max_pos */
+#define MLA_DEVERR_SEQ 2u      /* sequence id < 0 or >= num_seqs */
+#define MLA_DEVERR_BLOCK 4u    /* block-table entry < 0 or >= num_pool_blocks */
+#define MLA_DEVERR_LENGTH 8u   /* device lengths disagree with the host copies */
+
+typedef struct {
+  int32_t num_heads;   /* H */
+  int32_t d_latent;    /* d_c: latent (compressed KV) width, 512 for V3 */
+  int32_t d_rope;      /* d_r: decoupled RoPE width, 64 for V3 (even) */
+  int32_t d_nope;      /* d_n: no-RoPE query/key width per head, 128 for V3 */
+  int32_t d_v;         /* value width per head, 128 for V3 */
+  int32_t block_size;  /* tokens per cache block, 64 */
+  float softmax_scale; /* 1/sqrt(d_nope + d_rope) ([MLA explainer] "MLA的实现") */
+  int32_t dtype;       /* mla_dtype */
+} mla_config;
+
+/* Human-readable name of a status code (static string). */
+const char* mla_status_string(mla_status s);
+
+/* Host helper.  RoPE tables ([MLA explainer] "MLA的实现", RoPE module: inverse
+ * frequency theta^(-2i/d_rope), rotate-half pairing): for p < max_pos and
+ * i < d_rope/2, cos_host[p*(d_rope/2)+i] = cos(p * theta^(-2i/d_rope)) and likewise
+ * sin, evaluated in double precision and rounded once to float.  Host memory of
+ * max_pos*d_rope/2 floats each, owned by the caller; upload it for
+ * mla_append_cache.  INVALID_ARG for null pointers, max_pos < 1 or odd d_rope. */
+mla_status mla_rope_table(float* cos_host, float* sin_host, int32_t max_pos,
+                          int32_t d_rope, double theta);
+
+/* Query absorption ([MLA explainer] stage 2B / forward_inference_absorbed: the
+ * no-RoPE query is mapped through W_UK into the latent space; [MLA deep dive] 2.3):
+ *   q_lat[t][h][c] = round( sum_d q_nope[t][h][d] * w_uk[h][d][c] ),  c < d_latent
+ * fp32 accumulation, rounded to the storage dtype (nearest-even for bf16).  Writes
+ * columns [0, d_latent) of q_lat only; the RoPE columns are written by
+ * mla_append_cache.  T = 0 is a no-op.  Device pointers. */
+mla_status mla_absorb_q(const mla_config* cfg, int32_t T, const void* q_nope,
+                        const void* w_uk, void* q_lat, void* stream);
+
+/* Fused RoPE + latent-cache append ([MLA architecture] 4.2: RoPE fused with the
+ * cache update; 3.2: cache = latent part + shared RoPE key).  For each token t
+ * (sequence s = token_seq[t], position p = positions[t]):
+ *   row = block_table[s][p / block_size] * block_size + p % block_size
+ *   kv_pool[row][0:d_c]    = c_kv[t]                         (copied bit for bit)
+ *   kv_pool[row][d_c:d_c+d_r] = RoPE_p(k_pe[t])
+ *   q_lat[t][h][d_c:d_c+d_r]  = RoPE_p(q_pe[t][h])  for every head (if q_pe != NULL)
+ * RoPE_p(x): with half = d_r/2, c = rope_cos[p][i], s = rope_sin[p][i], i < half,
+ *   y[i] = x[i]*c - x[i+half]*s,  y[i+half] = x[i+half]*c + x[i]*s,
+ * computed in fp32 with every product and sum rounded to fp32 (no fused
+ * multiply-add), then rounded to the storage dtype (nearest-even).  The pool row
+ * is therefore bit-exact and independent of the device.
+ * rope_cos / rope_sin: device [max_pos][d_r/2] fp32 (e.g. from mla_rope_table).
+ * q_pe / q_lat may both be NULL (cache-only append, e.g. filling history).
+ * Entries with an out-of-range position, sequence id or block id are skipped and
+ * flagged in *dev_error (optional, device uint32, may be NULL).  Tokens that map
+ * to the same row race; the caller must not do that.  Device pointers. */
+mla_status mla_append_cache(const mla_config* cfg, int32_t T, const void* c_kv,
+                            const void* k_pe, const void* q_pe, const int32_t* token_seq,
+                            const int32_t* positions, const int32_t* block_table,
+                            int32_t num_seqs, int32_t max_blocks_per_seq,
+                            int64_t num_pool_blocks, const float* rope_cos,
+                            const float* rope_sin, int32_t max_pos, void* kv_pool,
+                            void* q_lat, uint32_t* dev_error, void* stream);
+
+/* Workspace bytes that mla_decode needs for this batch (split-KV partial results).
+ * Query tokens of sequence b are q_start[b] .. q_start[b+1]-1; the last of them is
+ * the token at position kv_lens[b]-1.  num_workgroups = 0 lets the library choose
+ * the split plan; a positive value forces that many KV workgroups (used to check
+ * that results do not depend on the split).  Host arrays.  INVALID_ARG when a
+ * length is < 1, a sequence has more query tokens than kv_len, or q_start is not
+ * non-decreasing from 0. */
+mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t num_seqs,
+                                     const int32_t* q_start_host,
+                                     const int32_t* kv_lens_host, int32_t causal,
+                                     int32_t num_workgroups, size_t* bytes);
+
+/* Absorbed latent attention over the paged cache ([MLA explainer] stage 2B and
+ * forward_inference_absorbed: latent score plus RoPE score, scaled, softmax,
+ * weighted sum of the cached latents; "MLA的常见问题" Q4: 512 + 64 asymmetric
+ * contraction).  For query token t of sequence b at position P = kv_lens[b] -
+ * (q_start[b+1]-q_start[b]) + j (j = t - q_start[b]) and every head h:
+ *   s_u = softmax_scale * sum_{k < d_c+d_r} q_lat[t][h][k] * row_u[k]
+ *   for cached positions u < kv_lens[b] (u <= P when causal != 0)
+ *   o_lat[t][h][c] = round( sum_u softmax(s)_u * row_u[c] ),  c < d_c
+ * Exact max-subtracted softmax, fp32 arithmetic, one rounding of o_lat to the
+ * storage dtype (split-KV partials are stored normalised in the storage dtype
+ * with an fp32 log-sum-exp and merged in fp32, in a fixed order: results are
+ * run-to-run bitwise deterministic for a given split plan).
+ * q_start, kv_lens, block_table: device; q_start_host, kv_lens_host: the same
+ * values on the host (used to plan the split without a device sync).
+ * workspace: device, at least mla_decode_workspace_size() bytes (may be NULL if
+ * that is 0).  dev_error: optional device word for MLA_DEVERR_* flags (a bad block
+ * id is skipped; the affected outputs are then undefined but no memory outside the
+ * given buffers is touched). */
+mla_status mla_decode(const mla_config* cfg, int32_t num_seqs, const int32_t* q_start,
+                      const int32_t* kv_lens, const int32_t* q_start_host,
+                      const int32_t* kv_lens_host, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, int64_t num_pool_blocks,
+                      const void* q_lat, const void* kv_pool, int32_t causal,
+                      int32_t num_workgroups, void* workspace, size_t workspace_bytes,
+                      void* o_lat, uint32_t* dev_error, void* stream);
+
+/* Per-head value up-projection ([MLA explainer] forward_inference_absorbed: the
+ * attended latent is mapped through W_UV per head, V is never formed):
+ *   out[t][h][v] = sum_c o_lat[t][h][c] * w_uv[h][v][c]   (fp32 accumulate, fp32 out)
+ * T = 0 is a no-op.  Device pointers. */
+mla_status mla_out_proj(const mla_config* cfg, int32_t T, const void* o_lat,
+                        const void* w_uv, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H_ */

@@ -1,0 +1,167 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same
+seeded inputs.  Bit-exact for the cache rows (and the RoPE columns of q_lat);
+within the stated tolerances for floating-point outputs."""
+import numpy as np
+import pytest
+import torch
+
+from head_latent_attention_05_amd import binding as B
+from head_latent_attention_05_amd import synth
+from head_latent_attention_05_amd.step import DeviceStep, to_device, to_host
+from oracle import mla_oracle as O
+from tests.gpu_util import check_out, oracle_pool, pool_bits, rows_fn, sample_heads
+
+pytestmark = pytest.mark.gpu
+
+# Small cases that still span several cache blocks and a ragged tail.
+SMALL = {
+    "tiny": dict(workload="tiny"),
+    "tiny_batch": dict(workload="tiny", kv_lens=[1, 63, 64, 65, 200], q_len=1),
+    "tiny_prefill": dict(workload="tiny", kv_lens=[150, 77], q_len=40, causal=True),
+    "v3_single_ragged": dict(workload="single", kv_lens=[1000]),
+    "v3_batch_ragged": dict(workload="batch64", kv_lens=[1, 64, 65, 700, 1333]),
+    "v3_prefill_small": dict(workload="prefill", kv_lens=[300, 170], q_len=130, causal=True),
+}
+
+
+def make(name):
+    spec = dict(SMALL[name])
+    wl = synth.WORKLOADS[spec.pop("workload")]
+    causal = spec.pop("causal", wl.causal)
+    if causal != wl.causal:
+        import dataclasses
+        wl = dataclasses.replace(wl, causal=causal)
+    return synth.make_inputs(wl, **spec)
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_append_bit_exact(name):
+    announce(f"append {name}")
+    inp = make(name)
+    st = DeviceStep(inp)
+    st.append()
+    torch.cuda.synchronize()
+    assert int(st.dev_error.item()) == 0
+    got = pool_bits(to_host(st.pool, inp.dims.dtype), inp.dims)
+    ref = pool_bits(oracle_pool(inp), inp.dims)
+    assert got.shape == ref.shape
+    np.testing.assert_array_equal(got, ref)  # includes the sentinel in unused rows
+    # RoPE columns of q_lat follow the same fp32 op order and rounding
+    d = inp.dims
+    cos, sin = O.rope_table_f32(inp.max_pos(), d.d_rope)
+    pos = inp.token_pos()
+    qpe = O.storage_to_f64(inp.q_pe, d.dtype).astype(np.float32)
+    exp = O.rope_cache_f32(qpe, cos[pos][:, None, :], sin[pos][:, None, :])
+    exp = O.to_bf16_bits(exp) if d.dtype == "bf16" else exp
+    got_q = to_host(st.q_lat, d.dtype)[:, :, d.d_latent:]
+    np.testing.assert_array_equal(pool_bits(got_q, d), pool_bits(exp, d))
+
+
+def test_append_flags_bad_entries():
+    announce("append error flags")
+    inp = make("tiny")
+    st = DeviceStep(inp)
+    before = to_host(st.pool, "f32").copy()
+    dev = st.dev
+    # position beyond the table, sequence id out of range, unassigned block
+    seq = torch.tensor([0, 5, 0], dtype=torch.int32, device=dev)
+    pos = torch.tensor([100000, 3, 127], dtype=torch.int32, device=dev)
+    bt = st.block_table.clone()
+    bt[0, 1] = -1
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ck = torch.zeros((3, inp.dims.d_latent), dtype=torch.float32, device=dev)
+    kp = torch.zeros((3, inp.dims.d_rope), dtype=torch.float32, device=dev)
+    B.append_cache(st.cfg, ck, kp, None, seq, pos, bt, st.num_blocks, st.rope_cos, st.rope_sin,
+                   st.pool, dev_error=err)
+    torch.cuda.synchronize()
+    e = int(err.item())
+    assert e & B.DEVERR_POSITION and e & B.DEVERR_SEQ and e & B.DEVERR_BLOCK
+    np.testing.assert_array_equal(to_host(st.pool, "f32").view(np.uint32), before.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["tiny", "v3_single_ragged", "v3_prefill_small"])
+def test_absorb_q(name):
+    announce(f"absorb_q {name}")
+    inp = make(name)
+    st = DeviceStep(inp)
+    st.absorb()
+    torch.cuda.synchronize()
+    d = inp.dims
+    ref = O.absorb_q(d, inp.q_nope, inp.w_uk)
+    got = O.storage_to_f64(to_host(st.q_lat, d.dtype), d.dtype)[:, :, :d.d_latent]
+    err = np.abs(got - ref)
+    if d.dtype == "bf16":  # one bf16 rounding of an fp32 sum
+        assert np.all(err <= np.abs(ref) * 2.0 ** -8 + 1e-6), err.max()
+    else:
+        assert err.max() <= 1e-5 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("name", ["tiny", "v3_single_ragged", "v3_batch_ragged"])
+def test_out_proj(name):
+    announce(f"out_proj {name}")
+    inp = make(name)
+    d = inp.dims
+    st = DeviceStep(inp)
+    o_np = synth.random_latent_outputs(d, inp.T, seed=11)
+    st.o_lat.copy_(to_device(o_np, d.dtype, st.dev))
+    st.project()
+    torch.cuda.synchronize()
+    ref = O.out_proj(d, O.storage_to_f64(o_np, d.dtype), inp.w_uv)
+    got = st.out.cpu().numpy()
+    assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def _decode_only(inp, st, q_np, num_workgroups):
+    st.num_workgroups = num_workgroups
+    nbytes = B.decode_workspace_size(st.cfg, st.q_start_host, st.kv_lens_host, st.causal,
+                                     num_workgroups)
+    st.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=st.dev) if nbytes else None
+    q = to_device(q_np, inp.dims.dtype, st.dev)
+    o = torch.full_like(st.o_lat, float("nan"))
+    st.decode(q_lat=q, o_lat=o)
+    torch.cuda.synchronize()
+    return O.storage_to_f64(to_host(o, inp.dims.dtype), inp.dims.dtype)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_latent_and_split_invariance(name):
+    inp = make(name)
+    d = inp.dims
+    st = DeviceStep(inp)
+    st.append()
+    q_np = synth.random_latent_queries(d, inp.T, seed=5)
+    pool = oracle_pool(inp)
+    heads = sample_heads(d.num_heads)
+    ref = O.latent_decode(d, O.storage_to_f64(q_np, d.dtype), rows_fn(pool, inp), inp.kv_lens,
+                          inp.q_start, inp.workload.causal, heads)
+    outs = {}
+    for G in (1, 2, 7, 0, 100000):
+        announce(f"decode {name} G={G}")
+        got = _decode_only(inp, st, q_np, G)
+        assert np.all(np.isfinite(got)), f"G={G}"
+        g = got[:, heads]
+        tol = (2.0 ** -7 if d.dtype == "bf16" else 1e-5) * np.abs(ref).max()
+        assert np.abs(g - ref).max() <= tol, (G, np.abs(g - ref).max(), tol)
+        outs[G] = got
+    # same plan twice -> bitwise identical
+    again = _decode_only(inp, st, q_np, 7)
+    np.testing.assert_array_equal(again, outs[7])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_full_step(name):
+    announce(f"step {name}")
+    inp = make(name)
+    st = DeviceStep(inp)
+    st.run()
+    torch.cuda.synchronize()
+    assert int(st.dev_error.item()) == 0
+    d = inp.dims
+    heads = sample_heads(d.num_heads, 8)
+    ref, _ = O.step(inp, heads)
+    got = st.out.cpu().numpy()[:, heads]
+    check_out(d, got, ref, name)
