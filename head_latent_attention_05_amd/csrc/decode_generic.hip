@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a, int H
   const S* pool = (const S*)a.pool;
   const S* qlat = (const S*)a.q_lat;
   const int bs = p.block_size;
-  TokenCursor c = locate_unit(p, u0);
+  TokenCursor c = locate_unit(p, (int)u0);
   bool first = true;
   while (true) {
     const int64_t seg_s = max(u0, c.ts), seg_e = min(u1, c.ts + c.nu);
@@ -115,8 +115,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int H, int dc)
   const int t = blockIdx.x;
   const PlanArgs& p = a.plan;
   const int b = seq_of_token(p, t);
-  const int64_t L = p.kv_lens[b];
-  const int64_t q = (int64_t)p.q_start[b + 1] - p.q_start[b];
+  const int L = p.kv_lens[b];
+  const int q = p.q_start[b + 1] - p.q_start[b];
   const int j = t - p.q_start[b];
   const int64_t ts = units_before_seq(p, b) + seq_units_before(L, q, j, p.block_size, p.causal);
   const int64_t nu = (attend_len(L, q, j, p.causal) + p.block_size - 1) / p.block_size;

@@ -13,6 +13,7 @@ hipError_t launch_absorb_generic(const mla_config& c, int T, const void* q_nope,
 hipError_t launch_out_proj_generic(const mla_config& c, int T, const void* o_lat,
                                    const void* w_uv, float* out, hipStream_t st);
 bool v3_kernels_available();
+bool v3_proj_available();
 
 namespace {
 
@@ -84,6 +85,7 @@ mla_status plan_decode(const mla_config& c, int32_t B, const int32_t* qs, const 
     if (q < 0 || L < 1 || q > L) return MLA_ERR_INVALID_ARG;
     U += seq_units_before(L, q, q, c.block_size, causal ? 1 : 0);
   }
+  if (U >= ((int64_t)1 << 31)) return MLA_ERR_UNSUPPORTED;  // unit indices are 32-bit
   hp->T = qs[B];
   hp->U = U;
   if (U == 0) {
@@ -154,7 +156,7 @@ mla_status mla_absorb_q(const mla_config* cfg, int32_t T, const void* q_nope, co
   if (!q_nope || !w_uk || !q_lat) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_lat)) return MLA_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
-  if (is_v3_bf16(*cfg) && v3_kernels_available()) return from_hip(launch_absorb_q(*cfg, T, q_nope, w_uk, q_lat, st));
+  if (is_v3_bf16(*cfg) && v3_proj_available()) return from_hip(launch_absorb_q(*cfg, T, q_nope, w_uk, q_lat, st));
   return from_hip(launch_absorb_generic(*cfg, T, q_nope, w_uk, q_lat, st));
 }
 
@@ -260,7 +262,7 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t T, const void* o_lat, con
   if (!o_lat || !w_uv || !out) return MLA_ERR_INVALID_ARG;
   if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
-  if (is_v3_bf16(*cfg) && v3_kernels_available()) return from_hip(launch_out_proj(*cfg, T, o_lat, w_uv, out, st));
+  if (is_v3_bf16(*cfg) && v3_proj_available()) return from_hip(launch_out_proj(*cfg, T, o_lat, w_uv, out, st));
   return from_hip(launch_out_proj_generic(*cfg, T, o_lat, w_uv, out, st));
 }
 
