@@ -22,6 +22,10 @@ FLAGS = [
     "-Wno-unused-function",
     # packed fp32 VALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep CFG simplification from merging stores to different fields of the
+    # decode kernel's tile-walker state behind a pointer phi, which would force
+    # that state into scratch memory
+    "-mllvm", "-simplifycfg-sink-common=false",
 ]
 
 
