@@ -48,17 +48,8 @@ class MlaConfig(ctypes.Structure):
                    MLA_BF16 if dims.dtype == "bf16" else MLA_F32)
 
 
-_lib = None
-
-
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libmla.so (built by head_latent_attention_05_amd.build)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(path):
-        raise ImportError(f"{path} is missing: run `python -m head_latent_attention_05_amd.build`")
-    lib = ctypes.CDLL(path)
+def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Set the ctypes signatures of the C ABI (include/mla.h) on a loaded library."""
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     C = ctypes.POINTER(MlaConfig)
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -75,6 +66,21 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode.argtypes = [C, I32, P, P, P, P, P, I32, I64, P, P, I32, I32, P, SZ, P, P, P]
     lib.mla_out_proj.restype = I32
     lib.mla_out_proj.argtypes = [C, I32, P, P, P, P]
+    return lib
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmla.so (built by head_latent_attention_05_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: run `python -m head_latent_attention_05_amd.build`")
+    lib = ctypes.CDLL(path)
+    declare(lib)
     _lib = lib
     return lib
 

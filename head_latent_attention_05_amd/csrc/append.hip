@@ -90,12 +90,12 @@ hipError_t launch_append(const mla_config& c, int T, const void* c_kv, const voi
                          void* q_lat, uint32_t* err, hipStream_t st) {
   dim3 grid(T), block(256);
   if (c.dtype == MLA_BF16) {
-    append_kernel<uint16_t><<<grid, block, 0, st>>>(
+    hipLaunchKernelGGL(append_kernel<uint16_t>, grid, block, 0, st,
         c.num_heads, c.d_latent, c.d_rope, c.block_size, (const uint16_t*)c_kv,
         (const uint16_t*)k_pe, (const uint16_t*)q_pe, seq, pos, bt, num_seqs, max_blocks,
         num_blocks, cosT, sinT, max_pos, (uint16_t*)pool, (uint16_t*)q_lat, err);
   } else {
-    append_kernel<float><<<grid, block, 0, st>>>(
+    hipLaunchKernelGGL(append_kernel<float>, grid, block, 0, st,
         c.num_heads, c.d_latent, c.d_rope, c.block_size, (const float*)c_kv, (const float*)k_pe,
         (const float*)q_pe, seq, pos, bt, num_seqs, max_blocks, num_blocks, cosT, sinT, max_pos,
         (float*)pool, (float*)q_lat, err);

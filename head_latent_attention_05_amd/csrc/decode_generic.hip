@@ -153,18 +153,20 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int H, int dc)
 hipError_t launch_decode_generic(const mla_config& c, const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.plan.G, (c.num_heads + 3) / 4), block(256);
   if (c.dtype == MLA_BF16)
-    decode_generic_kernel<uint16_t><<<grid, block, 0, st>>>(a, c.num_heads, c.d_latent, c.d_rope);
+    hipLaunchKernelGGL(decode_generic_kernel<uint16_t>, grid, block, 0, st, a, c.num_heads,
+                       c.d_latent, c.d_rope);
   else
-    decode_generic_kernel<float><<<grid, block, 0, st>>>(a, c.num_heads, c.d_latent, c.d_rope);
+    hipLaunchKernelGGL(decode_generic_kernel<float>, grid, block, 0, st, a, c.num_heads,
+                       c.d_latent, c.d_rope);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const mla_config& c, const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.plan.T, (c.num_heads + 3) / 4), block(256);
   if (c.dtype == MLA_BF16)
-    merge_kernel<uint16_t><<<grid, block, 0, st>>>(a, c.num_heads, c.d_latent);
+    hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, block, 0, st, a, c.num_heads, c.d_latent);
   else
-    merge_kernel<float><<<grid, block, 0, st>>>(a, c.num_heads, c.d_latent);
+    hipLaunchKernelGGL(merge_kernel<float>, grid, block, 0, st, a, c.num_heads, c.d_latent);
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@
 // transposing reads (32 lanes per cycle) hit 64 distinct banks.
 #include <math.h>
 
+#include "gfx950_asm.h"
 #include "plan_device.h"
 
 namespace mla {
@@ -48,12 +49,10 @@ constexpr int kChunksPerRow = kRowBytes / 16;            // 72
 constexpr int kTileChunks = kTile * kChunksPerRow;       // 2304
 constexpr int kTileBytes = kTileChunks * 16;             // 36864
 constexpr int kNBuf = 4;
-constexpr int kLoadsPerWave = kTileChunks / 256;         // 9 x 1 KiB per wave
 constexpr float kRescale = 8.0f;                         // lazy rescale threshold (log2)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-#define LDS_AS __attribute__((address_space(3)))
 
 static_assert(kTileChunks % 256 == 0, "tile must split evenly over 4 waves");
 
@@ -79,11 +78,6 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
   else
     __builtin_amdgcn_s_waitcnt(0x3f70);
 }
-
-// Workgroup barrier without the memory fence that __syncthreads implies (that
-// fence waits for every outstanding load, which would drain the tile pipeline);
-// the explicit wait_tiles() before it orders the LDS data.
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Per-tile descriptor handed from the loader walk to the compute loop.
 enum : int { kFirstOfSeg = 1 << 8, kLastOfSeg = 1 << 9, kWhole = 1 << 10, kBad = 1 << 11 };
@@ -146,33 +140,6 @@ struct Loader {
     fill(p, bt, stride, true);
   }
 };
-
-// One 16-byte-per-lane direct-to-LDS load: lane l's 16 bytes from base + voff
-// land at lds_dst + 16*l.  Written as inline asm so the compiler does not treat
-// every later LDS read as a possible reader of the in-flight data (it would then
-// wait for all outstanding loads before each tile); ordering is explicit
-// instead: wait_tiles() + barrier() before a tile is read.  The instruction has
-// no destination register; its address operands are read at issue.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is set here and used by nothing else
-__device__ __forceinline__ void dma16(const char* base_, uint32_t voff, char* lds_dst) {
-  // both addresses are wave-uniform; make that explicit for the scalar operands
-  // (readfirstlane yields a signed int: go through uint32_t so the low half is
-  // zero-extended, not sign-extended, when the pointer is rebuilt)
-  const uint64_t bv = (uint64_t)base_;
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bv);
-  const char* base = (const char*)((hi << 32) | lo);
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LDS_AS char*)lds_dst);
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(base), "s"(m0v)
-      : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Issue this wave's 9 direct-to-LDS loads of one tile.  Load i (0..35) moves the
 // latent part of row i (i < 32) or the RoPE parts of rows 8(i-32)..8(i-32)+7;
@@ -473,7 +440,7 @@ __global__ __launch_bounds__(256, 1) void decode_v3_kernel(
 bool v3_kernels_available() { return true; }
 
 hipError_t launch_decode_v3(const DecodeArgs& a, hipStream_t st) {
-  decode_v3_kernel<<<dim3(2 * a.plan.G), dim3(256), 0, st>>>(
+  hipLaunchKernelGGL(decode_v3_kernel, dim3(2 * a.plan.G), dim3(256), 0, st,
       a.plan.q_start, a.plan.kv_lens, a.block_table, (const uint16_t*)a.pool,
       (const uint16_t*)a.q_lat, (uint16_t*)a.o_lat, (uint16_t*)a.ws_o, a.ws_lse, a.err, a.plan.B,
       a.plan.T, a.plan.causal, a.plan.G, a.plan.U, a.max_blocks, a.num_blocks, a.scale_log2);

@@ -13,7 +13,6 @@ hipError_t launch_absorb_generic(const mla_config& c, int T, const void* q_nope,
 hipError_t launch_out_proj_generic(const mla_config& c, int T, const void* o_lat,
                                    const void* w_uv, float* out, hipStream_t st);
 bool v3_kernels_available();
-bool v3_proj_available();
 
 namespace {
 
@@ -155,12 +154,12 @@ mla_status mla_absorb_q(const mla_config* cfg, int32_t T, const void* q_nope, co
                         void* q_lat, void* stream) {
   mla_status s = check_cfg(cfg);
   if (s != MLA_OK) return s;
-  if (T < 0) return MLA_ERR_INVALID_ARG;
+  if (T < 0 || T > MLA_MAX_PROJ_TOKENS) return MLA_ERR_INVALID_ARG;
   if (T == 0) return MLA_OK;
   if (!q_nope || !w_uk || !q_lat) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_lat)) return MLA_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
-  if (is_v3_bf16(*cfg) && v3_proj_available()) return from_hip(launch_absorb_q(*cfg, T, q_nope, w_uk, q_lat, st));
+  if (is_v3_bf16(*cfg)) return from_hip(launch_absorb_q(*cfg, T, q_nope, w_uk, q_lat, st));
   return from_hip(launch_absorb_generic(*cfg, T, q_nope, w_uk, q_lat, st));
 }
 
@@ -261,12 +260,12 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t T, const void* o_lat, con
                         float* out, void* stream) {
   mla_status s = check_cfg(cfg);
   if (s != MLA_OK) return s;
-  if (T < 0) return MLA_ERR_INVALID_ARG;
+  if (T < 0 || T > MLA_MAX_PROJ_TOKENS) return MLA_ERR_INVALID_ARG;
   if (T == 0) return MLA_OK;
   if (!o_lat || !w_uv || !out) return MLA_ERR_INVALID_ARG;
   if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
-  if (is_v3_bf16(*cfg) && v3_proj_available()) return from_hip(launch_out_proj(*cfg, T, o_lat, w_uv, out, st));
+  if (is_v3_bf16(*cfg)) return from_hip(launch_out_proj(*cfg, T, o_lat, w_uv, out, st));
   return from_hip(launch_out_proj_generic(*cfg, T, o_lat, w_uv, out, st));
 }
 

@@ -86,13 +86,13 @@ hipError_t launch_absorb_generic(const mla_config& c, int T, const void* q_nope,
                                  const void* w_uk, void* q_lat, hipStream_t st) {
   dim3 grid((c.d_latent + 255) / 256, c.num_heads, (T + kTokTile - 1) / kTokTile), block(256);
   if (c.dtype == MLA_BF16)
-    absorb_generic_kernel<uint16_t><<<grid, block, 0, st>>>(
+    hipLaunchKernelGGL(absorb_generic_kernel<uint16_t>, grid, block, 0, st,
         T, c.num_heads, c.d_nope, c.d_latent, c.d_rope, (const uint16_t*)q_nope,
         (const uint16_t*)w_uk, (uint16_t*)q_lat);
   else
-    absorb_generic_kernel<float><<<grid, block, 0, st>>>(T, c.num_heads, c.d_nope, c.d_latent,
-                                                         c.d_rope, (const float*)q_nope,
-                                                         (const float*)w_uk, (float*)q_lat);
+    hipLaunchKernelGGL(absorb_generic_kernel<float>, grid, block, 0, st,
+        T, c.num_heads, c.d_nope, c.d_latent, c.d_rope, (const float*)q_nope,
+        (const float*)w_uk, (float*)q_lat);
   return hipGetLastError();
 }
 
@@ -100,10 +100,10 @@ hipError_t launch_out_proj_generic(const mla_config& c, int T, const void* o_lat
                                    const void* w_uv, float* out, hipStream_t st) {
   dim3 grid(c.num_heads, (T + kTokTile - 1) / kTokTile), block(256);
   if (c.dtype == MLA_BF16)
-    out_proj_generic_kernel<uint16_t><<<grid, block, 0, st>>>(
+    hipLaunchKernelGGL(out_proj_generic_kernel<uint16_t>, grid, block, 0, st,
         T, c.num_heads, c.d_latent, c.d_v, (const uint16_t*)o_lat, (const uint16_t*)w_uv, out);
   else
-    out_proj_generic_kernel<float><<<grid, block, 0, st>>>(
+    hipLaunchKernelGGL(out_proj_generic_kernel<float>, grid, block, 0, st,
         T, c.num_heads, c.d_latent, c.d_v, (const float*)o_lat, (const float*)w_uv, out);
   return hipGetLastError();
 }

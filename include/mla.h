@@ -79,6 +79,9 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
 #define MLA_DEVERR_BLOCK 4u    /* block-table entry < 0 or >= num_pool_blocks */
 #define MLA_DEVERR_LENGTH 8u   /* device lengths disagree with the host copies */
 
+/* Largest token count one mla_absorb_q / mla_out_proj call accepts. */
+#define MLA_MAX_PROJ_TOKENS 262144
+
 typedef struct {
   int32_t num_heads;   /* H */
   int32_t d_latent;    /* d_c: latent (compressed KV) width, 512 for V3 */
@@ -107,7 +110,8 @@ mla_status mla_rope_table(float* cos_host, float* sin_host, int32_t max_pos,
  *   q_lat[t][h][c] = round( sum_d q_nope[t][h][d] * w_uk[h][d][c] ),  c < d_latent
  * fp32 accumulation, rounded to the storage dtype (nearest-even for bf16).  Writes
  * columns [0, d_latent) of q_lat only; the RoPE columns are written by
- * mla_append_cache.  T = 0 is a no-op.  Device pointers. */
+ * mla_append_cache.  T = 0 is a no-op; T > MLA_MAX_PROJ_TOKENS is INVALID_ARG.
+ * Device pointers. */
 mla_status mla_absorb_q(const mla_config* cfg, int32_t T, const void* q_nope,
                         const void* w_uk, void* q_lat, void* stream);
 
@@ -177,7 +181,7 @@ mla_status mla_decode(const mla_config* cfg, int32_t num_seqs, const int32_t* q_
 /* Per-head value up-projection ([MLA explainer] forward_inference_absorbed: the
  * attended latent is mapped through W_UV per head, V is never formed):
  *   out[t][h][v] = sum_c o_lat[t][h][c] * w_uv[h][v][c]   (fp32 accumulate, fp32 out)
- * T = 0 is a no-op.  Device pointers. */
+ * T = 0 is a no-op; T > MLA_MAX_PROJ_TOKENS is INVALID_ARG.  Device pointers. */
 mla_status mla_out_proj(const mla_config* cfg, int32_t T, const void* o_lat,
                         const void* w_uv, float* out, void* stream);
 

@@ -1,0 +1,88 @@
+"""Builds the library's HIP sources as host C++ against the emulator runtime:
+tests/emu/_build/libmla_emu.so exports the same C ABI as libmla.so, with every
+kernel run on the CPU by the emulator.  Test infrastructure only.
+
+    python -m tests.emu.build_emu
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import glob
+import hashlib
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+CSRC = os.path.join(ROOT, "head_latent_attention_05_amd", "csrc")
+OUT_DIR = os.path.join(HERE, "_build")
+LIB = os.path.join(OUT_DIR, "libmla_emu.so")
+CXX = os.environ.get("EMU_CXX", "/opt/rocm/llvm/bin/clang++")
+
+FLAGS = [
+    "-std=c++17", "-O2", "-g", "-fPIC", "-Wall", "-Wno-unused-function",
+    "-Wno-unknown-pragmas", "-Wno-unused-variable", "-Wno-pass-failed",
+    "-fno-strict-aliasing",
+    # out-of-range indexing of fixed-size arrays (register tiles, LDS arrays) traps
+    "-fsanitize=bounds", "-fsanitize-trap=all",
+    "-I", os.path.join(HERE, "include"),
+]
+
+
+def _sources():
+    hips = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    return hips, [os.path.join(HERE, "emu_runtime.cpp")]
+
+
+def _stamp() -> str:
+    h = hashlib.sha256()
+    hips, cpps = _sources()
+    deps = hips + cpps + sorted(glob.glob(os.path.join(CSRC, "*.h")))
+    deps += sorted(glob.glob(os.path.join(HERE, "include", "**", "*.h"), recursive=True))
+    deps += [os.path.join(ROOT, "include", "mla.h"), os.path.abspath(__file__)]
+    for p in deps:
+        h.update(p.encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(FLAGS).encode())
+    return h.hexdigest()
+
+
+def _compile(args):
+    src, is_hip = args
+    obj = os.path.join(OUT_DIR, os.path.basename(src) + ".emu.o")
+    cmd = [CXX, *FLAGS]
+    if is_hip:
+        cmd += ["-x", "c++", "-include", "emu_gfx950_asm.h"]
+    cmd += ["-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"emulator build failed for {src}:\n{r.stderr}")
+    return obj
+
+
+def build(force: bool = False) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    stamp = _stamp()
+    stamp_file = os.path.join(OUT_DIR, "stamp")
+    if not force and os.path.exists(LIB) and os.path.exists(stamp_file):
+        with open(stamp_file) as f:
+            if f.read() == stamp:
+                return LIB
+    hips, cpps = _sources()
+    jobs = [(s, True) for s in hips] + [(s, False) for s in cpps]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(_compile, jobs))
+    tmp = LIB + ".tmp"
+    r = subprocess.run([CXX, "-shared", "-fPIC", "-o", tmp, *objs], capture_output=True,
+                       text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"emulator link failed:\n{r.stderr}")
+    os.replace(tmp, LIB)
+    with open(stamp_file, "w") as f:
+        f.write(stamp)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(force=True))

@@ -1,0 +1,30 @@
+// Emulator versions of the library's inline-asm helpers (csrc/gfx950_asm.h).
+// Force-included before a kernel source; defining that header's include guard
+// here makes the source use these definitions instead of the asm ones.
+#pragma once
+#define MLA_GFX950_ASM_H
+
+#include <stdint.h>
+#include <string.h>
+
+#include "hip/hip_runtime.h"
+
+#define LDS_AS __attribute__((address_space(3)))
+
+namespace mla {
+
+__forceinline__ void barrier() { ::emu::block_barrier(); }
+
+// lane l's 16 bytes from base + voff land at lds_dst + 16*l (completes at once)
+__forceinline__ void dma16(const char* base, uint32_t voff, char* lds_dst) {
+  // the instruction takes its base and LDS destination from scalar registers:
+  // they must be the same in every lane
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  if ((uint32_t)::emu::readfirstlane((unsigned)(b >> 32)) != (uint32_t)(b >> 32) ||
+      (uint32_t)::emu::readfirstlane((unsigned)b) != (uint32_t)b ||
+      ::emu::readfirstlane((unsigned)(uintptr_t)lds_dst) != (int)(unsigned)(uintptr_t)lds_dst)
+    ::emu::fail("dma16: base or LDS destination differs between lanes");
+  memcpy(lds_dst + 16 * ::emu::lane_id(), base + voff, 16);
+}
+
+}  // namespace mla

@@ -1,0 +1,123 @@
+// Host emulation of the HIP execution model, for compiling the library's kernel
+// sources as ordinary C++ and running them on the CPU in tests.
+//
+// Every work-item runs as a fiber on one OS thread.  A fiber runs until it
+// reaches a point where it must meet other work-items:
+//   - a wavefront collective (MFMA, cross-lane shuffles, ballot,
+//     readfirstlane, the transposing LDS read): all live lanes of the
+//     64-lane wave must arrive at the same collective, which is then computed
+//     for the whole wave at once;
+//   - a workgroup barrier: all live work-items of the group must arrive.
+// Between those points fibers run in a seeded random order, so a missing
+// barrier shows up as results that change with the seed.  Workgroups of a grid
+// run one after the other; `__shared__` variables become function statics
+// (one workgroup is live at a time).  Loads and stores are plain host memory
+// accesses: asynchronous copies complete at once, so the emulator checks
+// indexing, data movement and cross-lane layouts, not the timing of waits.
+//
+// Cross-lane layouts (gfx950, wave64):
+//   v_mfma_f32_16x16x32_bf16: lane l = 16g + i holds A[i][8g..8g+7] and
+//     B[8g..8g+7][i] (8 bf16 each) and D[4g..4g+3][i] (4 fp32);
+//   ds_read_b64_tr_b16: in each 16-lane group, lane j supplies 4 consecutive
+//     16-bit values src[j][0..3]; lane i receives src[4r + i/4][i%4], r = 0..3.
+#pragma once
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <functional>
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
+struct dim3 {
+  uint32_t x, y, z;
+  constexpr dim3(uint32_t x_ = 1, uint32_t y_ = 1, uint32_t z_ = 1) : x(x_), y(y_), z(z_) {}
+};
+
+namespace emu {
+
+constexpr int kWave = 64;
+
+struct LaneIO {
+  alignas(16) unsigned char in[64];
+  alignas(16) unsigned char out[64];
+};
+// A wave collective: io[l] is lane l's in/out block (null when lane l is not
+// live); `live` has bit l set for every live lane.
+typedef void (*WaveFn)(uint64_t live, LaneIO* const* io);
+
+extern dim3* g_tid;
+extern dim3 g_bid, g_bdim, g_gdim;
+
+int lane_id();
+void wave_op(WaveFn fn, const void* in, size_t nin, void* out, size_t nout);
+void block_barrier();
+void fail(const char* msg);
+void run_grid(dim3 grid, dim3 block, const std::function<void()>& body);
+
+void op_mfma_16x16x32_bf16(uint64_t live, LaneIO* const* io);
+void op_tr16_b64(uint64_t live, LaneIO* const* io);
+void op_gather(uint64_t live, LaneIO* const* io);
+void op_ballot(uint64_t live, LaneIO* const* io);
+void op_first(uint64_t live, LaneIO* const* io);
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+inline f32x4_t mfma_16x16x32_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  unsigned char in[48];
+  memcpy(in, &a, 16);
+  memcpy(in + 16, &b, 16);
+  memcpy(in + 32, &c, 16);
+  f32x4_t d;
+  wave_op(op_mfma_16x16x32_bf16, in, sizeof in, &d, sizeof d);
+  return d;
+}
+
+inline i16x4_t tr16_b64(const void* p) {
+  i16x4_t r;
+  wave_op(op_tr16_b64, &p, sizeof p, &r, sizeof r);
+  return r;
+}
+
+template <typename T>
+inline T gather(T v, int src) {
+  static_assert(sizeof(T) <= 8, "shuffle of at most 8 bytes");
+  unsigned char in[12] = {};
+  memcpy(in, &v, sizeof(T));
+  memcpy(in + 8, &src, 4);
+  unsigned char out[8];
+  wave_op(op_gather, in, sizeof in, out, sizeof out);
+  T r;
+  memcpy(&r, out, sizeof(T));
+  return r;
+}
+
+inline int readfirstlane(int v) {
+  int r;
+  wave_op(op_first, &v, sizeof v, &r, sizeof r);
+  return r;
+}
+inline int readfirstlane(unsigned v) { return readfirstlane((int)v); }
+
+// {own value, value of lane l ^ 16} / {own value, value of lane l ^ 32}
+inline u32x2_t permlane_swap(unsigned v, int mask) {
+  u32x2_t r;
+  r[0] = v;
+  r[1] = gather(v, lane_id() ^ mask);
+  return r;
+}
+
+template <typename... P, typename... A>
+void launch(void (*k)(P...), dim3 grid, dim3 block, A&&... args) {
+  // convert the arguments to the kernel's parameter types once, as a launch does
+  std::tuple<std::decay_t<P>...> packed(std::forward<A>(args)...);
+  run_grid(grid, block, [&]() { std::apply(k, packed); });
+}
+
+}  // namespace emu

@@ -83,7 +83,8 @@ def test_append_flags_bad_entries():
     np.testing.assert_array_equal(to_host(st.pool, "f32").view(np.uint32), before.view(np.uint32))
 
 
-@pytest.mark.parametrize("name", ["tiny", "v3_single_ragged", "v3_prefill_small"])
+@pytest.mark.parametrize("name", ["tiny", "v3_single_ragged", "v3_batch_ragged",
+                                  "v3_prefill_small"])
 def test_absorb_q(name):
     announce(f"absorb_q {name}")
     inp = make(name)
@@ -100,7 +101,8 @@ def test_absorb_q(name):
         assert err.max() <= 1e-5 * np.abs(ref).max()
 
 
-@pytest.mark.parametrize("name", ["tiny", "v3_single_ragged", "v3_batch_ragged"])
+@pytest.mark.parametrize("name", ["tiny", "v3_single_ragged", "v3_batch_ragged",
+                                  "v3_prefill_small"])
 def test_out_proj(name):
     announce(f"out_proj {name}")
     inp = make(name)
