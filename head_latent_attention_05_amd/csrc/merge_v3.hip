@@ -1,0 +1,88 @@
+// Merge of split-KV partial results for DeepSeek-V3 shapes (128 heads, 512
+// latent features, bf16 partials).
+//
+// A token whose cache blocks were split over KV ranges wlo..whi has, per range,
+// an output normalised over that range's rows and the log2-sum-exp of its
+// scaled scores.  The softmax over all rows is the lse-weighted mix:
+//   o = sum_w 2^(lse_w - M) o_w / sum_w 2^(lse_w - M),   M = max_w lse_w,
+// taken in increasing w, so results are deterministic for a split plan.  This
+// is the online-softmax identity that [MLA explainer] stage 2B's softmax
+// reduces to when its rows are processed in pieces.
+//
+// Workgroup = one token x 16 heads; thread = one head x 32 features (four
+// 16-byte loads per range, the next range's loads issued before the current
+// one is accumulated).  The token's unit range comes from one wave-parallel
+// pass over the sequences.
+#include <math.h>
+
+#include "plan_device.h"
+
+namespace mla {
+namespace {
+
+constexpr int kH = 128;
+constexpr int kDC = 512;
+
+__device__ __forceinline__ int64_t slot_of(int64_t w, int ts, const PlanArgs& p) {
+  return range_start(w, p.U, p.G) >= ts ? 2 * w : 2 * w + 1;
+}
+
+__device__ __forceinline__ void load4(const uint16_t* p, u32x4* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = ((const u32x4*)p)[i];
+}
+
+__global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* __restrict__ ws_lse,
+                                                       const uint16_t* __restrict__ ws_o,
+                                                       uint16_t* __restrict__ o_lat) {
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y * 16 + (tid >> 4);
+  const int f0 = (tid & 15) * 32;
+  int ts, nu;
+  locate_token(p, t, ts, nu);
+  const int64_t wlo = range_of(ts, p.U, p.G), whi = range_of((int64_t)ts + nu - 1, p.U, p.G);
+  if (wlo == whi) return;  // finished in place by one workgroup
+
+  float mx = -INFINITY;
+  for (int64_t w = wlo; w <= whi; ++w) mx = fmaxf(mx, ws_lse[slot_of(w, ts, p) * kH + h]);
+
+  float acc[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+  float den = 0.f;
+  u32x4 cur[4], nxt[4] = {};
+  load4(ws_o + (slot_of(wlo, ts, p) * kH + h) * kDC + f0, cur);
+  for (int64_t w = wlo; w <= whi; ++w) {
+    if (w < whi) load4(ws_o + (slot_of(w + 1, ts, p) * kH + h) * kDC + f0, nxt);
+    const float e = exp2f(ws_lse[slot_of(w, ts, p) * kH + h] - mx);
+    den += e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[8 * i + 2 * k] += e * __uint_as_float(cur[i][k] << 16);
+        acc[8 * i + 2 * k + 1] += e * __uint_as_float(cur[i][k] & 0xffff0000u);
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+  }
+  const float inv = 1.f / den;
+  u32x4* dst = (u32x4*)(o_lat + ((int64_t)t * kH + h) * kDC + f0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    dst[i] = u32x4{pack_bf16x2(acc[8 * i] * inv, acc[8 * i + 1] * inv),
+                   pack_bf16x2(acc[8 * i + 2] * inv, acc[8 * i + 3] * inv),
+                   pack_bf16x2(acc[8 * i + 4] * inv, acc[8 * i + 5] * inv),
+                   pack_bf16x2(acc[8 * i + 6] * inv, acc[8 * i + 7] * inv)};
+}
+
+}  // namespace
+
+hipError_t launch_merge_v3(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(merge_v3_kernel, dim3(a.plan.T, kH / 16), dim3(256), 0, st, a.plan,
+                     a.ws_lse, (const uint16_t*)a.ws_o, (uint16_t*)a.o_lat);
+  return hipGetLastError();
+}
+
+}  // namespace mla

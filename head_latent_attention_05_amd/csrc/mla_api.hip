@@ -252,7 +252,7 @@ mla_status mla_decode(const mla_config* cfg, int32_t num_seqs, const int32_t* q_
   else
     e = launch_decode_generic(*cfg, a, st);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  if (hp.G > 1) e = launch_merge(*cfg, a, st);
+  if (hp.G > 1) e = is_v3_bf16(*cfg) ? launch_merge_v3(a, st) : launch_merge(*cfg, a, st);
   return from_hip(e);
 }
 

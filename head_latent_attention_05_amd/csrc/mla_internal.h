@@ -123,5 +123,6 @@ struct DecodeArgs {
 hipError_t launch_decode_generic(const mla_config& c, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_v3(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_merge(const mla_config& c, const DecodeArgs& a, hipStream_t st);
+hipError_t launch_merge_v3(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace mla

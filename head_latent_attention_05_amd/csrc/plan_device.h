@@ -131,6 +131,42 @@ __device__ __forceinline__ void cursor_next(const PlanArgs& p, TokenCursor& c) {
   cursor_fill(p, c);
 }
 
+// First unit (ts) and unit count (nu) of global query token t, from one
+// wave-parallel pass over the sequences.  Wave-uniform results.
+__device__ inline void locate_token(const PlanArgs& p, int t, int& ts, int& nu) {
+  const int lane = threadIdx.x & 63;
+  int acc = 0, f_ts = 0, f_nu = 0;
+  for (int base = 0; base < p.B; base += 64) {
+    const int b = base + lane;
+    int qs0 = 0, qs1 = 0, L = 0, v = 0;
+    if (b < p.B) {
+      qs0 = ldc(p.q_start, b);
+      qs1 = ldc(p.q_start, b + 1);
+      L = ldc(p.kv_lens, b);
+      v = seq_units_upto(p, L, qs1 - qs0, qs1 - qs0);
+    }
+    const int incl = wave_incl_scan(v) + acc;
+    const bool mine = b < p.B && qs0 <= t && t < qs1;
+    const unsigned long long m = __ballot(mine);
+    if (m) {  // wave-uniform
+      int my_ts = 0, my_nu = 0;
+      if (mine) {
+        const int q = qs1 - qs0, j = t - qs0;
+        my_ts = incl - v + seq_units_upto(p, L, q, j);
+        const int A = p.causal ? L - q + j + 1 : L;
+        my_nu = (A + p.block_size - 1) / p.block_size;
+      }
+      const int l = __ffsll((long long)m) - 1;
+      f_ts = __shfl(my_ts, l, 64);
+      f_nu = __shfl(my_nu, l, 64);
+      break;
+    }
+    acc = __shfl(incl, 63, 64);
+  }
+  ts = uni(f_ts);
+  nu = uni(f_nu);
+}
+
 // Sequence index of global query token t (largest b with q_start[b] <= t).
 __device__ inline int seq_of_token(const PlanArgs& p, int t) {
   int lo = 0, hi = p.B - 1;
