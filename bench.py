@@ -111,8 +111,8 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(decode shards by sequence with no exchange; see DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (decode batches "
+              "would shard by sequence with no exchange).", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -133,21 +133,27 @@ def main() -> int:
     pools = st.pools
 
     def step(i, ev=None):
+        # ev: events before absorb / after absorb / after append / after decode / after out_proj
         p = pools[i % copies]
-        st.absorb()
-        st.append(p)
         if ev is not None:
             ev[0].record()
-        st.decode(p)
+        st.absorb()
         if ev is not None:
             ev[1].record()
+        st.append(p)
+        if ev is not None:
+            ev[2].record()
+        st.decode(p)
+        if ev is not None:
+            ev[3].record()
         st.project()
+        if ev is not None:
+            ev[4].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -158,15 +164,30 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / args.steps
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    call_ms = {name: [ev[k].elapsed_time(ev[k + 1]) for ev in evs]
+               for k, name in enumerate(["mla_absorb_q", "mla_append_cache", "mla_decode",
+                                         "mla_out_proj"])}
+    dec_ms = call_ms["mla_decode"]
     dec_avg = float(np.mean(dec_ms))
     log(f"[bench] step {ms*1e3:.1f} us (wall {wall/args.steps*1e6:.1f} us), decode avg "
         f"{dec_avg*1e3:.1f} us, p10 {np.percentile(dec_ms,10)*1e3:.1f} p90 "
-        f"{np.percentile(dec_ms,90)*1e3:.1f}")
+        f"{np.percentile(dec_ms,90)*1e3:.1f}; " +
+        ", ".join(f"{k} {np.mean(v)*1e3:.1f} us" for k, v in call_ms.items()))
     assert int(st.dev_error.item()) == 0
 
     esz = 2 if d.dtype == "bf16" else 4
-    dec_bytes = reads * d.row * esz + inp.T * d.num_heads * (d.row + d.d_latent) * esz
+    H, T = d.num_heads, inp.T
+    dec_bytes = reads * d.row * esz + T * H * (d.row + d.d_latent) * esz
+    # algorithmic bytes of the other calls: weights once plus activations in and out
+    call_bytes = {
+        "mla_absorb_q": (H * d.d_nope * d.d_latent + T * H * (d.d_nope + d.d_latent)) * esz,
+        "mla_append_cache": T * (2 * d.row + 2 * H * d.d_rope) * esz,
+        "mla_decode": dec_bytes,
+        "mla_out_proj": (H * d.d_v * d.d_latent + T * H * d.d_latent) * esz + T * H * d.d_v * 4,
+    }
+    calls = {k: {"avg_us": float(np.mean(v)) * 1e3, "algorithmic_bytes": int(call_bytes[k]),
+                 "gbs": call_bytes[k] / (float(np.mean(v)) * 1e-3) / 1e9}
+             for k, v in call_ms.items()}
     dec_flops = reads * 2 * d.num_heads * (d.row + d.d_latent)
     achieved_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
     achieved_tfs = dec_flops / (dec_avg * 1e-3) / 1e12
@@ -196,6 +217,7 @@ def main() -> int:
                      "mfma": {"achieved": achieved_tfs, "peak": MFMA_BF16_PEAK_TFS,
                               "unit": "TFLOP/s", "frac": achieved_tfs / MFMA_BF16_PEAK_TFS,
                               "algorithmic_flops": dec_flops}},
+        "calls": calls,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
