@@ -137,3 +137,34 @@ def test_emu_bad_entries_flagged(emu):
     st.block_table[1, 1] = -1
     st.decode()
     assert int(st.dev_error[0]) & B.DEVERR_BLOCK
+
+
+def _drop_queries(inp, zero):
+    """The same step with no query tokens for the sequences in `zero` (their
+    rows all become history); the other sequences' queries are unchanged."""
+    q_lens = inp.q_lens.copy()
+    keep = np.concatenate([np.full(int(q), b not in zero) for b, q in enumerate(inp.q_lens)])
+    q_lens[list(zero)] = 0
+    q_start = np.zeros(len(q_lens) + 1, np.int32)
+    q_start[1:] = np.cumsum(q_lens)
+    return dataclasses.replace(inp, q_lens=q_lens, q_start=q_start, q_nope=inp.q_nope[keep],
+                               q_pe=inp.q_pe[keep])
+
+
+@pytest.mark.parametrize("workload,causal,q_len", [("batch64", False, 1), ("prefill", True, 5)])
+def test_emu_sequences_without_queries(emu, workload, causal, q_len):
+    """Sequences with no query tokens in the batch (empty q_start ranges) are
+    skipped by the split plan, the merge and the projections."""
+    inp = _inputs(workload, causal=causal, kv_lens=[100, 64, 300, 1, 129], q_len=q_len)
+    inp = _drop_queries(inp, {1, 3})
+    d = inp.dims
+    for G in (0, 3, 100000):
+        st = EmuStep(emu, inp, num_workgroups=G)
+        st.run()
+        assert int(st.dev_error[0]) == 0
+        pool = oracle_pool(inp)
+        np.testing.assert_array_equal(pool_bits(st.pool, d), pool_bits(pool, d))
+        heads = [0, 63, 64, 127]
+        ref = O.naive_mla(d, inp.w_uk, inp.w_uv, inp.q_nope, inp.q_pe, rows_fn(pool, inp),
+                          inp.kv_lens, inp.q_start, causal, heads)
+        check_out(d, st.out[:, heads], ref, f"emu no-query seqs {workload} G={G}")
