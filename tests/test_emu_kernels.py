@@ -168,3 +168,45 @@ def test_emu_sequences_without_queries(emu, workload, causal, q_len):
         ref = O.naive_mla(d, inp.w_uk, inp.w_uv, inp.q_nope, inp.q_pe, rows_fn(pool, inp),
                           inp.kv_lens, inp.q_start, causal, heads)
         check_out(d, st.out[:, heads], ref, f"emu no-query seqs {workload} G={G}")
+
+
+def _random_case(rng, it):
+    """A random small batch: V3 bf16 or tiny fp32, causal or not, lengths near
+    tile and block edges or anywhere up to 400, some sequences without queries,
+    and a random split plan."""
+    v3 = rng.random() < 0.7
+    causal = rng.random() < 0.4
+    B = int(rng.integers(1, 7))
+    edges = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129]
+    lens = [int(rng.choice(edges)) if rng.random() < 0.5 else int(rng.integers(1, 400))
+            for _ in range(B)]
+    q_len = int(rng.choice([1, 2, 3, 17, 40])) if causal else 1
+    inp = _inputs("batch64" if v3 else "tiny", causal=causal, kv_lens=lens, q_len=q_len,
+                  seed=5000 + it)
+    zero = {b for b in range(B) if rng.random() < 0.2}
+    if zero and len(zero) < B:
+        inp = _drop_queries(inp, zero)
+    G = int(rng.choice([0, 1, 2, 3, 5, 8, 13, 64, 100000]))
+    return inp, G
+
+
+@pytest.mark.parametrize("it", range(12))
+def test_emu_decode_random_shapes(emu, it):
+    rng = np.random.default_rng(it)
+    inp, G = _random_case(rng, it)
+    d = inp.dims
+    emu.set_seed(int(rng.integers(1, 1 << 30)))
+    st = EmuStep(emu, inp, num_workgroups=G)
+    st.append()
+    q = synth.random_latent_queries(d, inp.T, seed=it)
+    st.q_lat[...] = q
+    st.decode()
+    emu.set_seed(1)
+    assert int(st.dev_error[0]) == 0
+    pool = oracle_pool(inp)
+    heads = [0, 1, d.num_heads - 1] + ([63, 64] if d.num_heads == 128 else [])
+    ref = O.latent_decode(d, O.storage_to_f64(q, d.dtype), rows_fn(pool, inp), inp.kv_lens,
+                          inp.q_start, inp.workload.causal, heads)
+    got = O.storage_to_f64(st.o_lat, d.dtype)[:, heads]
+    tol = (2.0 ** -7 if d.dtype == "bf16" else 1e-5) * np.abs(ref).max()
+    assert np.abs(got - ref).max() <= tol, (inp.kv_lens, inp.q_lens, G)
