@@ -90,6 +90,10 @@ def test_projection_argument_checks():
     assert lib.mla_absorb_q(ctypes.byref(c), 1, P(FAKE + 2), P(FAKE), P(FAKE), None) == 1
     assert lib.mla_out_proj(ctypes.byref(c), 0, None, None, None, None) == 0
     assert lib.mla_out_proj(ctypes.byref(c), 2, P(FAKE), P(FAKE + 8), P(FAKE), None) == 1
+    # token count above the limit the header documents
+    big = int(re.search(r"#define MLA_MAX_PROJ_TOKENS (\d+)", open(HEADER).read()).group(1)) + 1
+    assert lib.mla_absorb_q(ctypes.byref(c), big, P(FAKE), P(FAKE), P(FAKE), None) == 1
+    assert lib.mla_out_proj(ctypes.byref(c), big, P(FAKE), P(FAKE), P(FAKE), None) == 1
 
 
 def test_append_argument_checks():
