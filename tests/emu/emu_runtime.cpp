@@ -5,6 +5,7 @@
 #include <sys/mman.h>
 #include <unistd.h>
 
+#include <deque>
 #include <map>
 #include <random>
 #include <vector>
@@ -59,10 +60,18 @@ struct Lane {
 constexpr size_t kStackBytes = 512 * 1024;
 constexpr size_t kPage = 4096;
 
+// One direct-to-LDS load instruction of a wave that has not landed yet.
+struct DmaOp {
+  char* dst;                 // LDS address of lane 0's 16 bytes
+  const char* src[kWave];    // global source of each lane's 16 bytes
+  uint64_t live;
+};
+
 struct Wave {
   int live = 0;     // lanes not finished
   int arrived = 0;  // lanes waiting at the current collective
   WaveFn fn = nullptr;
+  std::deque<DmaOp> dma;  // issued, not yet landed (oldest first)
 };
 
 std::vector<Lane> g_lanes;
@@ -73,6 +82,7 @@ int g_at_barrier = 0;
 void* g_sched_sp = nullptr;
 Lane* g_cur = nullptr;
 const std::function<void()>* g_body = nullptr;
+int g_op_wave = -1;  // wave whose collective is being computed
 std::mt19937_64 g_rng(1);
 int g_cus = 8;
 unsigned long long g_wave_ops = 0, g_barriers = 0, g_blocks = 0;
@@ -122,7 +132,9 @@ void complete_wave(int w, int nlanes) {
     live |= 1ull << l;
     io[l] = &L.io;
   }
+  g_op_wave = w;
   W.fn(live, io);
+  g_op_wave = -1;
   ++g_wave_ops;
   for (int l = 0; l < n; ++l)
     if (live >> l & 1) {
@@ -198,6 +210,18 @@ void run_block(int nlanes) {
   if (g_live != 0)
     fail("workgroup cannot make progress: a wave waits at a collective that some of its "
          "lanes never reach, or some work-items wait at a barrier others never reach");
+  // loads still in flight when the workgroup ends write LDS nobody reads again
+  for (Wave& W : g_waves) W.dma.clear();
+}
+
+// Lands the oldest direct-to-LDS loads of wave W until at most `keep` remain.
+void land_dma(Wave& W, size_t keep) {
+  while (W.dma.size() > keep) {
+    const DmaOp& op = W.dma.front();
+    for (int l = 0; l < kWave; ++l)
+      if (op.live >> l & 1) memcpy(op.dst + 16 * l, op.src[l], 16);
+    W.dma.pop_front();
+  }
 }
 
 }  // namespace
@@ -319,6 +343,34 @@ void op_first(uint64_t live, LaneIO* const* io) {
   const int f = __builtin_ctzll(live);
   for (int l = 0; l < kWave; ++l)
     if (live >> l & 1) memcpy(io[l]->out, io[f]->in, 4);
+}
+
+// Direct-to-LDS load: queued; the loads of a wave land in issue order, mostly
+// as late as the s_waitcnt that requires them (so a wait that is too weak shows
+// up as stale LDS data), sometimes right after they are issued (so a load into
+// a buffer that is still being read shows up too).
+void op_dma16(uint64_t live, LaneIO* const* io) {
+  Wave& W = g_waves[g_op_wave];
+  DmaOp op;
+  op.live = live;
+  op.dst = nullptr;
+  for (int l = 0; l < kWave; ++l) {
+    op.src[l] = nullptr;
+    if (!(live >> l & 1)) continue;
+    char* dst;
+    memcpy(&op.src[l], io[l]->in, sizeof(void*));
+    memcpy(&dst, io[l]->in + 8, sizeof(void*));
+    if (op.dst && dst != op.dst) fail("direct-to-LDS load: LDS base differs between lanes");
+    op.dst = dst;
+  }
+  W.dma.push_back(op);
+  if (g_rng() % 8 == 0) land_dma(W, g_rng() % (W.dma.size() + 1));
+}
+
+void op_waitcnt(uint64_t live, LaneIO* const* io) {
+  int vm;
+  memcpy(&vm, io[__builtin_ctzll(live)]->in, 4);
+  land_dma(g_waves[g_op_wave], (size_t)vm);
 }
 
 }  // namespace emu

@@ -15,16 +15,16 @@ namespace mla {
 
 __forceinline__ void barrier() { ::emu::block_barrier(); }
 
-// lane l's 16 bytes from base + voff land at lds_dst + 16*l (completes at once)
+// lane l's 16 bytes from base + voff land at lds_dst + 16*l, asynchronously:
+// only an s_waitcnt vmcnt that counts this load guarantees they have landed
 __forceinline__ void dma16(const char* base, uint32_t voff, char* lds_dst) {
   // the instruction takes its base and LDS destination from scalar registers:
   // they must be the same in every lane
   const uint64_t b = (uint64_t)(uintptr_t)base;
   if ((uint32_t)::emu::readfirstlane((unsigned)(b >> 32)) != (uint32_t)(b >> 32) ||
-      (uint32_t)::emu::readfirstlane((unsigned)b) != (uint32_t)b ||
-      ::emu::readfirstlane((unsigned)(uintptr_t)lds_dst) != (int)(unsigned)(uintptr_t)lds_dst)
-    ::emu::fail("dma16: base or LDS destination differs between lanes");
-  memcpy(lds_dst + 16 * ::emu::lane_id(), base + voff, 16);
+      (uint32_t)::emu::readfirstlane((unsigned)b) != (uint32_t)b)
+    ::emu::fail("dma16: base differs between lanes");
+  ::emu::dma16(base + voff, lds_dst);
 }
 
 }  // namespace mla

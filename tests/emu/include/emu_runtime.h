@@ -12,8 +12,10 @@
 // barrier shows up as results that change with the seed.  Workgroups of a grid
 // run one after the other; `__shared__` variables become function statics
 // (one workgroup is live at a time).  Loads and stores are plain host memory
-// accesses: asynchronous copies complete at once, so the emulator checks
-// indexing, data movement and cross-lane layouts, not the timing of waits.
+// accesses, except the direct-to-LDS loads: those are queued per wave and land
+// in issue order, mostly only when an s_waitcnt vmcnt requires them, so a wait
+// count that is too weak leaves stale LDS data behind.  Timing itself is not
+// modelled.
 //
 // Cross-lane layouts (gfx950, wave64):
 //   v_mfma_f32_16x16x32_bf16: lane l = 16g + i holds A[i][8g..8g+7] and
@@ -63,6 +65,8 @@ void op_tr16_b64(uint64_t live, LaneIO* const* io);
 void op_gather(uint64_t live, LaneIO* const* io);
 void op_ballot(uint64_t live, LaneIO* const* io);
 void op_first(uint64_t live, LaneIO* const* io);
+void op_dma16(uint64_t live, LaneIO* const* io);
+void op_waitcnt(uint64_t live, LaneIO* const* io);
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -111,6 +115,23 @@ inline u32x2_t permlane_swap(unsigned v, int mask) {
   r[0] = v;
   r[1] = gather(v, lane_id() ^ mask);
   return r;
+}
+
+// Direct-to-LDS load of 16 bytes per lane (lane l's bytes land at
+// lds_base + 16*l): asynchronous, see op_dma16.
+inline void dma16(const char* src, char* lds_base) {
+  unsigned char in[16], out[1];
+  memcpy(in, &src, 8);
+  memcpy(in + 8, &lds_base, 8);
+  wave_op(op_dma16, in, sizeof in, out, 0);
+}
+
+// s_waitcnt: waits until at most vmcnt of the wave's direct-to-LDS loads are
+// in flight (the other counters have nothing to wait for here).
+inline void s_waitcnt(int imm) {
+  const int vm = (imm & 0xf) | (((imm >> 14) & 3) << 4);
+  unsigned char out[1];
+  wave_op(op_waitcnt, &vm, sizeof vm, out, 0);
 }
 
 template <typename... P, typename... A>

@@ -34,7 +34,11 @@ hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int dev)
 #define hipLaunchKernelGGL(kernel, grid, block, shmem, stream, ...) \
   ::emu::launch(kernel, dim3(grid), dim3(block), ##__VA_ARGS__)
 
-inline void __syncthreads() { ::emu::block_barrier(); }
+// a full barrier also waits for every outstanding load of the wave
+inline void __syncthreads() {
+  ::emu::s_waitcnt(0);
+  ::emu::block_barrier();
+}
 
 template <typename A, typename B>
 inline typename std::common_type<A, B>::type min(A a, B b) {
@@ -117,6 +121,6 @@ inline unsigned long long __ballot(int pred) {
 #define __builtin_amdgcn_readfirstlane(x) ::emu::readfirstlane(x)
 #define __builtin_amdgcn_permlane16_swap(a, b, fi, bc) ::emu::permlane_swap((a), 16)
 #define __builtin_amdgcn_permlane32_swap(a, b, fi, bc) ::emu::permlane_swap((a), 32)
-#define __builtin_amdgcn_s_waitcnt(x) ((void)0)
+#define __builtin_amdgcn_s_waitcnt(x) ::emu::s_waitcnt(x)
 #define __builtin_amdgcn_sched_barrier(x) ((void)0)
 #define __builtin_amdgcn_s_setprio(x) ((void)0)

@@ -40,6 +40,9 @@ CASES = {
     "tiny_prefill": dict(workload="tiny", kv_lens=[150, 77], q_len=40, causal=True),
     "v3_batch_ragged": dict(workload="batch64", kv_lens=[70, 129, 1, 64, 200]),
     "v3_prefill_small": dict(workload="prefill", kv_lens=[150, 77], q_len=40),
+    # long segments: tiles stream through the loads-in-flight pipeline for many
+    # iterations, so the wait counts are exercised
+    "v3_long_segments": dict(workload="batch64", kv_lens=[2000, 700]),
 }
 
 
@@ -59,7 +62,8 @@ def test_emu_step(emu, name):
     check_out(d, st.out[:, heads], ref, f"emu {name}")
 
 
-@pytest.mark.parametrize("name", ["tiny_prefill", "v3_batch_ragged", "v3_prefill_small"])
+@pytest.mark.parametrize("name", ["tiny_prefill", "v3_batch_ragged", "v3_prefill_small",
+                                  "v3_long_segments"])
 def test_emu_decode_splits(emu, name):
     """Every split plan (forced 1, 2, 7 and more workgroups than units) against
     the oracle's latent decode; the same plan twice, and under another
