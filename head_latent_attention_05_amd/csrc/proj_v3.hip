@@ -69,9 +69,11 @@ __global__ __launch_bounds__(256) void absorb_v3_kernel(int T, const uint16_t* _
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    // rows past the last token repeat the last token: a token's outputs depend
+    // on its own row only, and those columns are not stored (no branch or select
+    // on the loads, so all of them are in flight at once)
     const int k = tid + 256 * i, r = k >> 4, c = k & 15;
-    qv[i] = t0 + r < T ? *(const u32x4*)(q_nope + ((int64_t)(t0 + r) * kH + h) * kDN + c * 8)
-                       : u32x4{0u, 0u, 0u, 0u};
+    qv[i] = *(const u32x4*)(q_nope + ((int64_t)min(t0 + r, T - 1) * kH + h) * kDN + c * 8);
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -159,8 +161,8 @@ __global__ __launch_bounds__(256) void out_proj_v3_kernel(int T, const uint16_t*
   for (int i = 0; i < 16; ++i) {
     const int k = tid + 256 * i, r = k >> 6, c = k & 63;
     wv[i] = *(const u32x4*)(wsrc + r * kDC + c * 8);
-    ov[i] = t0 + r < T ? *(const u32x4*)(o_lat + ((int64_t)(t0 + r) * kH + h) * kDC + c * 8)
-                       : u32x4{0u, 0u, 0u, 0u};
+    // rows past the last token repeat the last token (their outputs are not stored)
+    ov[i] = *(const u32x4*)(o_lat + ((int64_t)min(t0 + r, T - 1) * kH + h) * kDC + c * 8);
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
