@@ -10,9 +10,8 @@
 // reduces to when its rows are processed in pieces.
 //
 // Workgroup = one token x 16 heads; thread = one head x 32 features (four
-// 16-byte loads per range, the next range's loads issued before the current
-// one is accumulated).  The token's unit range comes from one wave-parallel
-// pass over the sequences.
+// 16-byte loads per range, four ranges' loads in flight together).  The
+// token's unit range comes from one wave-parallel pass over the sequences.
 #include <math.h>
 
 #include "plan_device.h"
@@ -44,28 +43,42 @@ __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* 
   const int64_t wlo = range_of(ts, p.U, p.G), whi = range_of((int64_t)ts + nu - 1, p.U, p.G);
   if (wlo == whi) return;  // finished in place by one workgroup
 
+  // Ranges are taken four at a time with branch-free loads (indices past the
+  // last range repeat it and get weight 0), so a token's partials are all in
+  // flight together for up to four ranges.
   float mx = -INFINITY;
-  for (int64_t w = wlo; w <= whi; ++w) mx = fmaxf(mx, ws_lse[slot_of(w, ts, p) * kH + h]);
+  for (int64_t w = wlo; w <= whi; w += 4) {
+    float l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l[j] = ws_lse[slot_of(min(w + j, whi), ts, p) * kH + h];
+    mx = fmaxf(mx, fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])));
+  }
 
   float acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = 0.f;
   float den = 0.f;
-  u32x4 cur[4], nxt[4] = {};
-  load4(ws_o + (slot_of(wlo, ts, p) * kH + h) * kDC + f0, cur);
-  for (int64_t w = wlo; w <= whi; ++w) {
-    if (w < whi) load4(ws_o + (slot_of(w + 1, ts, p) * kH + h) * kDC + f0, nxt);
-    const float e = exp2f(ws_lse[slot_of(w, ts, p) * kH + h] - mx);
-    den += e;
+  for (int64_t w = wlo; w <= whi; w += 4) {
+    u32x4 x[4][4];
+    float l[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int64_t slot = slot_of(min(w + j, whi), ts, p);
+      load4(ws_o + (slot * kH + h) * kDC + f0, x[j]);
+      l[j] = ws_lse[slot * kH + h];
+    }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[8 * i + 2 * k] += e * __uint_as_float(cur[i][k] << 16);
-        acc[8 * i + 2 * k + 1] += e * __uint_as_float(cur[i][k] & 0xffff0000u);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const float e = w + j <= whi ? exp2f(l[j] - mx) : 0.f;
+      den += e;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[8 * i + 2 * k] += e * __uint_as_float(x[j][i][k] << 16);
+          acc[8 * i + 2 * k + 1] += e * __uint_as_float(x[j][i][k] & 0xffff0000u);
+        }
+    }
   }
   const float inv = 1.f / den;
   u32x4* dst = (u32x4*)(o_lat + ((int64_t)t * kH + h) * kDC + f0);
