@@ -22,8 +22,12 @@ namespace {
 constexpr int kH = 128;
 constexpr int kDC = 512;
 
-__device__ __forceinline__ int64_t slot_of(int64_t w, int ts, const PlanArgs& p) {
-  return range_start(w, p.U, p.G) >= ts ? 2 * w : 2 * w + 1;
+// Partial slot of range w for a token whose first unit is ts, among the ranges
+// wlo..whi that touch it: a range after wlo starts inside the token, so the
+// token is that range's first segment (slot 2w); range wlo holds it as its
+// first segment (2w) only if it starts exactly at ts, else as its last (2w+1).
+__device__ __forceinline__ int64_t slot_of(int64_t w, int64_t wlo, int64_t slot_lo) {
+  return w == wlo ? slot_lo : 2 * w;
 }
 
 __device__ __forceinline__ void load4(const uint16_t* p, u32x4* x) {
@@ -42,6 +46,7 @@ __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* 
   locate_token(p, t, ts, nu);
   const int64_t wlo = range_of(ts, p.U, p.G), whi = range_of((int64_t)ts + nu - 1, p.U, p.G);
   if (wlo == whi) return;  // finished in place by one workgroup
+  const int64_t slot_lo = range_start(wlo, p.U, p.G) == ts ? 2 * wlo : 2 * wlo + 1;
 
   // Ranges are taken four at a time with branch-free loads (indices past the
   // last range repeat it and get weight 0), so a token's partials are all in
@@ -50,7 +55,7 @@ __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* 
   for (int64_t w = wlo; w <= whi; w += 4) {
     float l[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) l[j] = ws_lse[slot_of(min(w + j, whi), ts, p) * kH + h];
+    for (int j = 0; j < 4; ++j) l[j] = ws_lse[slot_of(min(w + j, whi), wlo, slot_lo) * kH + h];
     mx = fmaxf(mx, fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])));
   }
 
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* 
     float l[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t slot = slot_of(min(w + j, whi), ts, p);
+      const int64_t slot = slot_of(min(w + j, whi), wlo, slot_lo);
       load4(ws_o + (slot * kH + h) * kDC + f0, x[j]);
       l[j] = ws_lse[slot * kH + h];
     }
