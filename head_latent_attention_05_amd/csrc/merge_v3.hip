@@ -21,6 +21,7 @@ namespace {
 
 constexpr int kH = 128;
 constexpr int kDC = 512;
+constexpr int kBS = 64;
 
 // Partial slot of range w for a token whose first unit is ts, among the ranges
 // wlo..whi that touch it: a range after wlo starts inside the token, so the
@@ -38,6 +39,7 @@ __device__ __forceinline__ void load4(const uint16_t* p, u32x4* x) {
 __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* __restrict__ ws_lse,
                                                        const uint16_t* __restrict__ ws_o,
                                                        uint16_t* __restrict__ o_lat) {
+  p.block_size = kBS;  // a compile-time block size turns the unit arithmetic into shifts
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int h = blockIdx.y * 16 + (tid >> 4);
