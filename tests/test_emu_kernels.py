@@ -10,6 +10,7 @@ Timing and memory ordering are not emulated: waits and fences are checked on
 the GPU only.
 """
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -17,12 +18,15 @@ import pytest
 from head_latent_attention_05_amd import binding as B
 from head_latent_attention_05_amd import synth
 from oracle import mla_oracle as O
+from tests.emu import build_emu
 from tests.emu.emulib import Emu, EmuStep
 from tests.gpu_util import check_out, oracle_pool, pool_bits, rows_fn, sample_heads
 
 
 @pytest.fixture(scope="module")
 def emu():
+    if not os.path.exists(build_emu.CXX):
+        pytest.skip(f"host compiler {build_emu.CXX} not found")
     e = Emu(cus=8, seed=1)
     yield e
     e.close()
