@@ -14,8 +14,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped (not failed) where no GPU is visible; the round-end
-    # GPU run selects them with -m gpu on a box that has one.
+    # GPU tests are skipped (not failed) where no GPU is visible; on a machine
+    # with an MI355X they are selected with -m gpu.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
