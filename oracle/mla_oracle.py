@@ -18,7 +18,7 @@ Sources (web pages; cited by page and section):
 * [MLA deep dive]  mlqm.cn/news/500296 -- 2.3 (weight absorption), 5.1 (paged
   cache in serving frameworks).
 
-Readings where the pages are silent (listed with reasons in the design notes):
+Readings where the pages are silent:
 rotate-half RoPE pairing with theta 10000; 0-based positions; scale
 1/sqrt(d_nope + d_rope); exact max-subtracted softmax; causal mask for new
 tokens; cache rows hold [c_kv | RoPE(k_pe)] in storage precision; the RoPE of
