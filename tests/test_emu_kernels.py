@@ -218,3 +218,24 @@ def test_emu_decode_random_shapes(emu, it):
     got = O.storage_to_f64(st.o_lat, d.dtype)[:, heads]
     tol = (2.0 ** -7 if d.dtype == "bf16" else 1e-5) * np.abs(ref).max()
     assert np.abs(got - ref).max() <= tol, (inp.kv_lens, inp.q_lens, G)
+
+
+@pytest.mark.parametrize("causal,q_len", [(False, 1), (True, 3)])
+def test_emu_more_than_64_sequences(emu, causal, q_len):
+    """Batches wider than one wave: the plan walk and the merge scan the
+    sequences 64 at a time."""
+    lens = [int(x) for x in np.random.default_rng(7).integers(1, 100, size=90)]
+    inp = _inputs("batch64", causal=causal, kv_lens=lens, q_len=q_len, seed=11)
+    d = inp.dims
+    st = EmuStep(emu, inp)
+    st.append()
+    q = synth.random_latent_queries(d, inp.T, seed=3)
+    st.q_lat[...] = q
+    pool = oracle_pool(inp)
+    heads = [0, 64, 127]
+    ref = O.latent_decode(d, O.storage_to_f64(q, d.dtype), rows_fn(pool, inp), inp.kv_lens,
+                          inp.q_start, causal, heads)
+    for G in (0, 7, 100000):
+        st.decode(G)
+        got = O.storage_to_f64(st.o_lat, d.dtype)[:, heads]
+        assert np.abs(got - ref).max() <= 2.0 ** -7 * np.abs(ref).max(), G
