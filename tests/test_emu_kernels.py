@@ -239,3 +239,46 @@ def test_emu_more_than_64_sequences(emu, causal, q_len):
         st.decode(G)
         got = O.storage_to_f64(st.o_lat, d.dtype)[:, heads]
         assert np.abs(got - ref).max() <= 2.0 ** -7 * np.abs(ref).max(), G
+
+
+def _scale_rows(inp, f):
+    """The same step with every cached row of sequence b (c_kv and k_pe) scaled
+    by f(b, position): drives the logits over a wide range."""
+    c_kv, k_pe = [], []
+    for b in range(len(inp.kv_lens)):
+        s = np.array([f(b, p) for p in range(int(inp.kv_lens[b]))], np.float64)[:, None]
+        cf = synth.bf16_bits_to_f32(inp.c_kv[b]).astype(np.float64) * s
+        kf = synth.bf16_bits_to_f32(inp.k_pe[b]).astype(np.float64) * s
+        c_kv.append(synth.f32_to_bf16_bits(cf.astype(np.float32)))
+        k_pe.append(synth.f32_to_bf16_bits(kf.astype(np.float32)))
+    return dataclasses.replace(inp, c_kv=c_kv, k_pe=k_pe)
+
+
+@pytest.mark.parametrize("profile", ["rising", "falling", "sink"])
+def test_emu_decode_wide_logit_range(emu, profile):
+    """Logits that rise along the sequence (the running maximum grows by far
+    more than the lazy-rescale threshold, many times, and by more than the fp32
+    exponent range overall), fall (the maximum is found first), or have one
+    dominant row in the middle."""
+    inp = _inputs("batch64", kv_lens=[700, 333])
+    L = inp.kv_lens
+    # logit spread grows to ~60x the unit spread: without rescaling, 2^(s - m)
+    # would overflow fp32 long before the end of the rising sequence
+    f = {"rising": lambda b, p: 1.0 + 60.0 * p / L[b],
+         "falling": lambda b, p: 61.0 - 60.0 * p / L[b],
+         "sink": lambda b, p: 12.0 if p == L[b] // 2 else 1.0}[profile]
+    inp = _scale_rows(inp, f)
+    d = inp.dims
+    st = EmuStep(emu, inp)
+    st.append()
+    q = synth.random_latent_queries(d, inp.T, seed=9)
+    st.q_lat[...] = q
+    pool = oracle_pool(inp)
+    heads = [0, 17, 64, 127]
+    ref = O.latent_decode(d, O.storage_to_f64(q, d.dtype), rows_fn(pool, inp), inp.kv_lens,
+                          inp.q_start, False, heads)
+    for G in (1, 0, 5):
+        st.decode(G)
+        got = O.storage_to_f64(st.o_lat, d.dtype)[:, heads]
+        assert np.all(np.isfinite(got))
+        assert np.abs(got - ref).max() <= 2.0 ** -7 * np.abs(ref).max(), (profile, G)
