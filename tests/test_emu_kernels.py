@@ -282,3 +282,15 @@ def test_emu_decode_wide_logit_range(emu, profile):
         got = O.storage_to_f64(st.o_lat, d.dtype)[:, heads]
         assert np.all(np.isfinite(got))
         assert np.abs(got - ref).max() <= 2.0 ** -7 * np.abs(ref).max(), (profile, G)
+
+
+def test_emu_step_without_any_query(emu):
+    """A batch with no query tokens at all: every call is a no-op that leaves
+    its outputs untouched (only the history rows are in the cache)."""
+    inp = _drop_queries(_inputs("batch64", kv_lens=[70, 129]), {0, 1})
+    assert inp.T == 0
+    st = EmuStep(emu, inp)
+    st.run()
+    pool = oracle_pool(inp)
+    np.testing.assert_array_equal(pool_bits(st.pool, inp.dims), pool_bits(pool, inp.dims))
+    assert int(st.dev_error[0]) == 0
