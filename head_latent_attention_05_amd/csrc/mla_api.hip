@@ -222,6 +222,8 @@ mla_status mla_decode(const mla_config* cfg, int32_t num_seqs, const int32_t* q_
   for (int b = 0; b < num_seqs; ++b) maxL = kv_lens_host[b] > maxL ? kv_lens_host[b] : maxL;
   if (max_blocks_per_seq < (maxL + cfg->block_size - 1) / cfg->block_size)
     return MLA_ERR_INVALID_ARG;
+  // block-table entries are addressed with 32-bit indices on the device
+  if ((int64_t)num_seqs * max_blocks_per_seq >= ((int64_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
   if (hp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < hp.ws_bytes || !aligned16(workspace))
       return MLA_ERR_WORKSPACE;

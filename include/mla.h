@@ -169,7 +169,8 @@ mla_status mla_decode_workspace_size(const mla_config* cfg, int32_t num_seqs,
  * workspace: device, at least mla_decode_workspace_size() bytes (may be NULL if
  * that is 0).  dev_error: optional device word for MLA_DEVERR_* flags (a bad block
  * id is skipped; the affected outputs are then undefined but no memory outside the
- * given buffers is touched). */
+ * given buffers is touched).  UNSUPPORTED when the split plan has 2^31 or more
+ * (token, block) units or the block table has 2^31 or more entries. */
 mla_status mla_decode(const mla_config* cfg, int32_t num_seqs, const int32_t* q_start,
                       const int32_t* kv_lens, const int32_t* q_start_host,
                       const int32_t* kv_lens_host, const int32_t* block_table,

@@ -160,3 +160,10 @@ def test_decode_rejects_small_workspace_before_launch():
                         P(FAKE), 63, 100, P(FAKE), P(FAKE), 0, 8, P(FAKE), 1 << 30, P(FAKE),
                         None, None)
     assert st == 1
+    # block table with 2^31 entries or more: its device indices are 32-bit
+    qs2 = np.array([0, 1, 2], np.int32)
+    kl2 = np.array([4096, 4096], np.int32)
+    st = lib.mla_decode(ctypes.byref(c), 2, P(FAKE), P(FAKE), qs2.ctypes.data, kl2.ctypes.data,
+                        P(FAKE), 1 << 30, 100, P(FAKE), P(FAKE), 0, 8, P(FAKE), 1 << 30,
+                        P(FAKE), None, None)
+    assert st == 2
