@@ -101,7 +101,7 @@ def cpu_baseline(workload: str, budget_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batch64")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -185,7 +185,11 @@ def main() -> int:
         "mla_decode": dec_bytes,
         "mla_out_proj": (H * d.d_v * d.d_latent + T * H * d.d_latent) * esz + T * H * d.d_v * 4,
     }
-    calls = {k: {"avg_us": float(np.mean(v)) * 1e3, "algorithmic_bytes": int(call_bytes[k]),
+    calls = {k: {"avg_us": float(np.mean(v)) * 1e3,
+                 "p10_us": float(np.percentile(v, 10)) * 1e3,
+                 "p50_us": float(np.percentile(v, 50)) * 1e3,
+                 "p90_us": float(np.percentile(v, 90)) * 1e3,
+                 "algorithmic_bytes": int(call_bytes[k]),
                  "gbs": call_bytes[k] / (float(np.mean(v)) * 1e-3) / 1e9}
              for k, v in call_ms.items()}
     dec_flops = reads * 2 * d.num_heads * (d.row + d.d_latent)
