@@ -1,0 +1,492 @@
+// Split-KV absorbed latent attention for DeepSeek-V3 shapes on gfx950 MFMA.
+//
+// [MLA explainer] stage 2B / forward_inference_absorbed: per head, score =
+// (q_lat . c_kv + q_pe . k_pe) * scale, softmax over the cached rows, o_lat =
+// sum p * c_kv.  All 128 heads read the same cached row of 576 values
+// ([MLA architecture] section 1, 3.2).  "MLA的常见问题" Q4: the contraction is
+// 512 + 64 deep and does not fit square attention tiles; here a row is one
+// 576-deep contraction for the scores, and its first 512 columns are the values.
+//
+// One workgroup per KV range of the split plan, all 128 heads, 8 waves: every
+// cache tile goes from HBM into this CU's LDS exactly once.  The waves form two
+// teams of four; team T owns heads 64T..64T+63.  Per 32-token tile a team runs
+// two phases:
+//   S: wave k scores heads 64T+16k..+15:
+//        S^T[32 tok x 16 heads] = K[32 x 576] . Q^T[576 x 16] (36 MFMA 16x16x32),
+//        K rows read from LDS, Q^T held in registers for the query token;
+//      online softmax (a lane owns one head and 8 tokens, max / sum across the
+//      4 lanes of a head with permlane swaps, lazy rescaling);
+//      P^T (bf16) and the rescale factors of the team's heads go to LDS.
+//   P: wave k multiplies the values of features 128k..128k+127 for the team's
+//      64 heads: O^T[128 x 64] += V^T[128 x 32 tok] . P^T[32 tok x 64] (32 MFMA),
+//      V^T from the same LDS tile through the transposing read ds_read_b64_tr_b16.
+// The teams are half a tile apart: while team 0 scores tile i, team 1 runs the
+// value product of tile i-1, and the other way round in the next phase.  Each
+// SIMD holds one wave of each team, so one wave's MFMAs overlap the other's
+// LDS reads and softmax, and the K reads of the score phase are spread over
+// both phases.  A workgroup barrier separates phases.
+//
+// Tiles (half cache blocks, 32 rows, 36 KiB) stream HBM -> LDS with
+// direct-to-LDS loads (global_load_lds_dwordx4) into four buffers; every wave
+// loads its own rows.  Team 0 issues its share of tile i+3 in phase 2i+1, team 1
+// its share of tile i+2 in phase 2i, so two to two-and-a-half tiles are in
+// flight.  A wave whose next score phase starts a new query token loads that
+// token's Q during its value phase (its Q registers are idle then).
+//
+// LDS tile layout: the 32 latent rows (1 KiB each) then the 32 RoPE rows (128 B
+// each); 16-byte chunks are XOR-swizzled per row so that the score reads (16
+// rows x one chunk per LDS cycle) and the transposing reads hit distinct banks.
+#include <math.h>
+
+#include "gfx950_asm.h"
+#include "plan_device.h"
+
+namespace mla {
+namespace {
+
+constexpr int kH = 128;
+constexpr int kDC = 512;
+constexpr int kRow = 576;
+constexpr int kBS = 64;
+constexpr int kTile = 32;
+constexpr int kRowBytes = kRow * 2;                // 1152
+constexpr int kLatBytes = kDC * 2;                 // 1024: latent part of a row
+constexpr int kRopeBytes = kRowBytes - kLatBytes;  // 128: RoPE part of a row
+constexpr int kTileBytes = kTile * kRowBytes;      // 36864
+constexpr int kRegionB = kTile * kLatBytes;        // 32768: start of the RoPE region
+constexpr int kNBuf = 4;
+constexpr int kWaves = 8;
+constexpr float kRescale = 8.0f;  // lazy rescale threshold (log2 units)
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Chunk swizzles.  Latent region: chunk c of row t sits at c ^ fa(t); RoPE
+// region: chunk c of row t sits at c ^ fb(t).  fa only touches chunk bits 1..3.
+__device__ __forceinline__ int fa(int t) { return (t & 7) << 1; }
+__device__ __forceinline__ int fb(int t) { return (t >> 1) & 7; }
+
+// s_waitcnt with vmcnt = n (other counters unconstrained).  The instruction
+// takes an immediate, so a wave-uniform count is dispatched through a switch.
+__device__ __forceinline__ void wait_vm(int n) {
+#define MLA_VM(N) \
+  case N: __builtin_amdgcn_s_waitcnt(0x3f70 | ((N) & 0xf) | (((N) >> 4) << 14)); break;
+  switch (n) {
+    MLA_VM(0) MLA_VM(1) MLA_VM(2) MLA_VM(3) MLA_VM(4) MLA_VM(5) MLA_VM(6) MLA_VM(7)
+    MLA_VM(8) MLA_VM(9) MLA_VM(10) MLA_VM(11) MLA_VM(12) MLA_VM(13) MLA_VM(14) MLA_VM(15)
+    MLA_VM(16) MLA_VM(17) MLA_VM(18) MLA_VM(19) MLA_VM(20) MLA_VM(21) MLA_VM(22) MLA_VM(23)
+    MLA_VM(24) MLA_VM(25) MLA_VM(26) MLA_VM(27) MLA_VM(28) MLA_VM(29) MLA_VM(30) MLA_VM(31)
+    MLA_VM(32) MLA_VM(33) MLA_VM(34) MLA_VM(35) MLA_VM(36) MLA_VM(37) MLA_VM(38) MLA_VM(39)
+    MLA_VM(40) MLA_VM(41) MLA_VM(42) MLA_VM(43) MLA_VM(44) MLA_VM(45) MLA_VM(46) MLA_VM(47)
+    default: __builtin_amdgcn_s_waitcnt(0x3f70 | 0xf | (3 << 14)); break;  // 63
+  }
+#undef MLA_VM
+}
+
+// Per-tile descriptor flags (low byte: valid rows of the tile).
+enum : int {
+  kFirstOfSeg = 1 << 8,   // first tile of a query token within this range
+  kLastOfSeg = 1 << 9,    // last tile of a query token within this range
+  kWhole = 1 << 10,       // the token's rows all lie in this range: write o_lat
+  kBad = 1 << 11,         // block-table entry out of range: skipped
+  kSecondSlot = 1 << 12,  // not the range's first token: partial goes to slot 2w+1
+};
+
+// Walks the tiles (half cache blocks) of one workgroup's unit range in order.
+// Every field is wave-uniform.  The block-table entry of a block is read when
+// the walk enters it, one tile ahead of its issue for the second half.
+struct Loader {
+  TokenCursor c;
+  int u1;
+  int ub, ub_beg, ub_end;  // block range of the current segment (within the token)
+  int half;
+  int rows;     // valid rows of the current block
+  int nvalid;   // valid rows of the current tile (1..32)
+  int blk_raw;  // block-table entry of the current block
+  int valid;
+  int first;    // first tile of a segment
+  int nseg;     // segments entered so far
+
+  __device__ __forceinline__ void fill(const PlanArgs& p, const int32_t* bt, int stride,
+                                       bool new_block) {
+    const int A = p.causal ? c.L - c.q + c.j + 1 : c.L;
+    rows = uni(min(kBS, A - ub * kBS));
+    nvalid = min(kTile, rows - kTile * half);
+    if (new_block) blk_raw = ldc(bt, c.b * stride + ub);  // host keeps B*stride < 2^31
+  }
+  __device__ __forceinline__ void init(const PlanArgs& p, const int32_t* bt, int stride, int u0,
+                                       int u1_) {
+    u1 = u1_;
+    c = locate_unit(p, u0);
+    ub = ub_beg = u0 - c.ts;
+    ub_end = uni(min(u1, c.ts + c.nu) - c.ts);
+    half = 0;
+    valid = 1;
+    first = 1;
+    nseg = 0;
+    fill(p, bt, stride, true);
+  }
+  __device__ __forceinline__ bool last_of_segment() const {
+    return ub == ub_end - 1 && (half == 1 || rows <= kTile);
+  }
+  __device__ __forceinline__ bool whole_token() const { return ub_beg == 0 && ub_end == c.nu; }
+  __device__ __forceinline__ void next(const PlanArgs& p, const int32_t* bt, int stride) {
+    first = 0;
+    if (half == 0 && rows > kTile) {
+      half = 1;
+      fill(p, bt, stride, false);
+      return;
+    }
+    half = 0;
+    ++ub;
+    if (ub == ub_end) {
+      if (c.ts + c.nu >= u1) {
+        valid = 0;
+        return;
+      }
+      cursor_next(p, c);
+      ub = ub_beg = 0;
+      ub_end = uni(min(u1, c.ts + c.nu) - c.ts);
+      first = 1;
+      ++nseg;
+    }
+    fill(p, bt, stride, true);
+  }
+};
+
+// This wave's direct-to-LDS loads of one tile: latent rows W, W+8, W+16, W+24
+// (one 1 KiB load each) and, for waves 0-3, the RoPE parts of rows 8W..8W+7.
+// Rows past the end of a partial tile repeat its last valid row (their scores
+// are masked; repeating keeps every value finite).
+template <int W>
+__device__ __forceinline__ void issue_rows(const char* blk, int last, char* buf, int lane) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = W + 8 * r;
+    dma16(blk + min(i, last) * kRowBytes, (uint32_t)((lane ^ fa(i)) << 4), buf + i * kLatBytes);
+  }
+  if (W < 4) {
+    const int t = 8 * W + (lane >> 3);
+    const uint32_t voff = min(t, last) * kRowBytes + kLatBytes + (((lane & 7) ^ fb(t)) << 4);
+    dma16(blk, voff, buf + kRegionB + W * 1024);
+  }
+}
+
+__device__ __forceinline__ void issue_rows_w(int wave, const char* blk, int last, char* buf,
+                                             int lane) {
+  switch (wave) {
+    case 0: issue_rows<0>(blk, last, buf, lane); break;
+    case 1: issue_rows<1>(blk, last, buf, lane); break;
+    case 2: issue_rows<2>(blk, last, buf, lane); break;
+    case 3: issue_rows<3>(blk, last, buf, lane); break;
+    case 4: issue_rows<4>(blk, last, buf, lane); break;
+    case 5: issue_rows<5>(blk, last, buf, lane); break;
+    case 6: issue_rows<6>(blk, last, buf, lane); break;
+    default: issue_rows<7>(blk, last, buf, lane); break;
+  }
+}
+
+// max / sum over the 4 lanes that share a head (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float head_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float head_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+struct Shared {
+  char tiles[kNBuf][kTileBytes];
+  u32x4 pbuf[2][4][64];     // P^T fragments [team][head block][lane]
+  float alpha[2][4][16];    // rescale factor [team][head block][head % 16]
+  float invl[2][4][16];     // 1 / softmax denominator, same layout
+  int desc[kWaves][kNBuf][2];  // per wave: [tile % 4] = {flags | valid rows, token}
+};
+
+__global__ __launch_bounds__(512, 1) void decode_v4_kernel(
+    const int32_t* __restrict__ q_start, const int32_t* __restrict__ kv_lens,
+    const int32_t* __restrict__ block_table, const uint16_t* __restrict__ pool,
+    const uint16_t* __restrict__ qlat, uint16_t* __restrict__ o_lat, uint16_t* __restrict__ ws_o,
+    float* __restrict__ ws_lse, uint32_t* __restrict__ err, int B, int T, int causal, int G,
+    int64_t U, int max_blocks, int64_t num_blocks, float sl2) {
+  __shared__ __attribute__((aligned(1024))) Shared sh;
+  const int lane = threadIdx.x & 63;
+  const int wave = uni(threadIdx.x >> 6);
+  const int team = wave >> 2, wk = wave & 3;
+  PlanArgs p;
+  p.q_start = q_start;
+  p.kv_lens = kv_lens;
+  p.B = B;
+  p.T = T;
+  p.block_size = kBS;
+  p.causal = causal;
+  p.G = G;
+  p.U = U;
+  if (!plan_consistent(p, max_blocks)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0 && err) atomicOr(err, MLA_DEVERR_LENGTH);
+    return;
+  }
+  // Block ids are dealt round-robin over the 8 XCDs; consecutive ranges (which
+  // share a split token, its query and its partials) go to one XCD.
+  int w = blockIdx.x;
+  if ((G & 7) == 0) w = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int u0 = (int)range_start(w, U, G), u1 = (int)range_start(w + 1, U, G);
+  if (u0 >= u1) return;
+
+  const int l16 = lane & 15;  // MFMA column (head) / row index
+  const int g4 = lane >> 4;   // 16-lane group
+  const int shead = 64 * team + 16 * wk + l16;  // head this lane scores
+
+  // LDS addresses, as byte offsets from the start of the shared block.  Tile
+  // buffers are 4 KiB aligned there and the swizzles only touch offset bits
+  // 4..7, so an offset is (tile base + per-lane part) ^ (a constant selecting
+  // the chunk): no per-chunk offsets are kept in registers.
+  const char* lds0 = (const char*)&sh;
+  //   score reads (A operand = K rows): row l16 (+16 rows for the second token
+  //   block), latent chunk 4kk + g4 -> (lat_lane ^ ((kk & 3) << 6)) + 256 (kk >> 2),
+  //   RoPE chunk 4r + g4 (kk = 16 + r) -> rope_lane ^ (r << 6);
+  //   transposing reads (A operand = V^T) of feature block 8wk + f: rows
+  //   4g4 + (l16 >> 2) (+16), features 16(8wk + f) + 4(l16 & 3), i.e. chunk
+  //   16wk + 2f + ((l16 >> 1) & 1) -> val_lane ^ (f << 5).
+  const int faL = fa(l16), fbL = fb(l16);
+  const int lat_lane = l16 * kLatBytes + (((faL >> 2) & 3) << 6) + ((g4 ^ (faL & 2)) << 4);
+  const int rope_lane = kRegionB + l16 * kRopeBytes + ((g4 ^ fbL) << 4);
+  const int trow = 4 * g4 + (l16 >> 2);
+  const int val_lane = trow * kLatBytes + ((fa(trow) >> 1) << 5) + (((l16 >> 1) & 1) << 4) +
+                       8 * (l16 & 1) + wk * 256;
+  // global offsets (bytes) of this lane: query row of head shead, columns 8g4..
+  const int q_lane = (shead * kRow + 8 * g4) * 2;
+
+  const char* pool_b = (const char*)pool;
+  const int nmine = wave < 4 ? 5 : 4;  // direct-to-LDS loads per tile of this wave
+  Loader lg;
+  lg.init(p, block_table, max_blocks, u0, u1);
+  int issued = 0;  // tiles this wave has issued
+
+  u32x4 qreg[18];
+  f32x4 acc[8][4];  // [feature block][head block]
+  float m_run = -INFINITY, l_part = 0.f;
+
+  auto issue = [&]() {
+    const int k_ = issued % kNBuf;
+    const int bad_ = uni(lg.blk_raw < 0 || lg.blk_raw >= num_blocks);
+    const int phys_ = uni(bad_ ? 0 : lg.blk_raw);
+    const char* blk_ = pool_b + ((int64_t)phys_ * kBS + lg.half * kTile) * kRowBytes;
+    issue_rows_w(wave, blk_, bad_ ? 0 : lg.nvalid - 1, sh.tiles[k_], lane);
+    if (lane == 0) {
+      sh.desc[wave][k_][0] = (bad_ ? 0 : lg.nvalid) | (lg.first ? kFirstOfSeg : 0) |
+                             (lg.last_of_segment() ? kLastOfSeg : 0) |
+                             (lg.whole_token() ? kWhole : 0) | (bad_ ? kBad : 0) |
+                             (lg.nseg > 0 ? kSecondSlot : 0);
+      sh.desc[wave][k_][1] = lg.c.t;
+    }
+    lg.next(p, block_table, max_blocks);
+    ++issued;
+  };
+  auto desc_of = [&](int i) { return uni(sh.desc[wave][i % kNBuf][0]); };
+  auto tok_of = [&](int i) { return uni(sh.desc[wave][i % kNBuf][1]); };
+  // Q^T operand of this lane: head shead, columns 32kk + 8g4 .. +7.  The wait
+  // for it drains this wave's tiles in flight as well (loads complete in
+  // order); it sits right here so the compiler knows no load into qreg is
+  // pending anywhere else and adds no waits of its own inside the tile loop.
+  auto load_q = [&](int tok) {
+    const char* qb = (const char*)qlat + (int64_t)tok * (kH * kRow * 2) + opaque(q_lane);
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) qreg[kk] = *(const u32x4*)(qb + 64 * kk);
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+  };
+
+  // ---------------------------------------------------------------- S phase
+  auto score_phase = [&](int i) {
+    const int d = desc_of(i);
+    const char* tb = sh.tiles[i % kNBuf];
+    if (d & kFirstOfSeg) {
+      m_run = -INFINITY;
+      l_part = 0.f;
+    }
+    f32x4 s0 = {}, s1 = {};
+    u32x4 ka[2][2];  // K operands of k-steps kk and kk+1
+    const uint32_t la = opaque((uint32_t)(tb - lds0) + lat_lane);
+    const uint32_t ra = opaque((uint32_t)(tb - lds0) + rope_lane);
+    auto ld = [&](int kk, u32x4* dst) {
+      const uint32_t a = kk < 16 ? (la ^ ((kk & 3) << 6)) + (kk >> 2) * 256 : ra ^ ((kk - 16) << 6);
+      const int second = kk < 16 ? 16 * kLatBytes : 16 * kRopeBytes;
+      dst[0] = *(const u32x4*)(lds0 + a);
+      dst[1] = *(const u32x4*)(lds0 + a + second);
+    };
+    ld(0, ka[0]);
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) {
+      if (kk + 1 < 18) ld(kk + 1, ka[(kk + 1) & 1]);
+      const bf16x8 qb = __builtin_bit_cast(bf16x8, qreg[kk]);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kk & 1][0]), qb,
+                                                   s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kk & 1][1]), qb,
+                                                   s1, 0, 0, 0);
+    }
+    // online softmax: lane holds head l16, tokens 4g4+r (s0) and 16+4g4+r (s1).
+    // Weights are 2^(s*scale*log2(e) - m) on the hardware exp2 (v_exp_f32, ~1 ulp;
+    // arguments below -126 flush to 0, which is below bf16 resolution of P anyway).
+    const int nvalid = d & 0xff;
+    if ((d & kBad) && lane == 0 && err) atomicOr(err, MLA_DEVERR_BLOCK);
+    if (nvalid < kTile) {
+      const int lim = nvalid - 4 * g4;  // rows 4g4 + r of s0 are valid for r < lim
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (r >= lim) s0[r] = -INFINITY;
+        if (r >= lim - 16) s1[r] = -INFINITY;
+      }
+    }
+    const float mx = head_max(fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                                    fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))));
+    const float mt = mx * sl2;
+    float alpha = 1.f;
+    if (mt > m_run + kRescale) {
+      alpha = __builtin_amdgcn_exp2f(m_run - mt);
+      m_run = mt;
+      l_part *= alpha;
+    }
+    float pr[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, -m_run));
+      pr[4 + r] = __builtin_amdgcn_exp2f(fmaf(s1[r], sl2, -m_run));
+    }
+    l_part += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+    // P^T fragment of head block wk: k slots 0..3 = tokens 4g4+r, 4..7 = 16+4g4+r
+    sh.pbuf[team][wk][lane] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                    pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+    if (g4 == 0) sh.alpha[team][wk][l16] = alpha;
+    if (d & kLastOfSeg) {
+      const float l_tot = head_sum(l_part);
+      if (g4 == 0) sh.invl[team][wk][l16] = __builtin_amdgcn_rcpf(l_tot);
+      if (!(d & kWhole)) {
+        const int slot = 2 * w + ((d & kSecondSlot) ? 1 : 0);
+        const buf_t lse = buf_rsrc((char*)ws_lse + (int64_t)uni(slot) * (kH * 4), kH * 4);
+        // the lane offset is rebuilt here rather than kept live for this rare store
+        const uint32_t tid = opaque(threadIdx.x);
+        const uint32_t hd = ((tid >> 8) << 6) + (((tid >> 6) & 3) << 4) + (tid & 15);
+        if (g4 == 0)
+          buf_store_b32(__float_as_uint(m_run + __builtin_amdgcn_logf(l_tot)), lse, 4 * hd, 0);
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- P phase
+  auto value_phase = [&](int i) {
+    const int d = desc_of(i);
+    const char* tb = sh.tiles[i % kNBuf];
+    if (d & kFirstOfSeg) {
+#pragma unroll
+      for (int f = 0; f < 8; ++f)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) acc[f][h] = f32x4{};
+    } else {
+      const f32x4 al = {sh.alpha[team][0][l16], sh.alpha[team][1][l16], sh.alpha[team][2][l16],
+                        sh.alpha[team][3][l16]};
+      const bool resc = (al[0] != 1.f) | (al[1] != 1.f) | (al[2] != 1.f) | (al[3] != 1.f);
+      if (__ballot(resc) != 0) {
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) acc[f][h] *= al[h];
+      }
+    }
+    bf16x8 pb[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.pbuf[team][h][lane]);
+    const uint32_t va0 = opaque((uint32_t)(tb - lds0) + val_lane);
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const char* vp = lds0 + (va0 ^ (f << 5));
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)vp);
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + 16 * kLatBytes));
+      const bf16x8 va =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        acc[f][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[h], acc[f][h], 0, 0, 0);
+    }
+    if (d & kLastOfSeg) {
+      const f32x4 inv = {sh.invl[team][0][l16], sh.invl[team][1][l16], sh.invl[team][2][l16],
+                         sh.invl[team][3][l16]};
+      uint16_t* base;
+      if (d & kWhole) {
+        base = o_lat + (int64_t)tok_of(i) * kH * kDC;
+      } else {
+        const int slot = 2 * w + ((d & kSecondSlot) ? 1 : 0);
+        base = ws_o + (int64_t)uni(slot) * kH * kDC;
+      }
+      // lane holds features 16(8wk+f) + 4g4 + r of head 64team + 16h + l16
+      const buf_t out = buf_rsrc(base, kH * kDC * 2);
+      const uint32_t voff = opaque(((64 * team + l16) * kDC + 128 * wk + 4 * g4) * 2);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+          buf_store_b64(pack_bf16x2(acc[f][h][0] * inv[h], acc[f][h][1] * inv[h]),
+                        pack_bf16x2(acc[f][h][2] * inv[h], acc[f][h][3] * inv[h]), out, voff,
+                        16 * h * kDC * 2 + 32 * f);
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- schedule
+  // Phase 2i: team 0 scores tile i, team 1 multiplies the values of tile i-1;
+  // phase 2i+1: team 0 multiplies the values of tile i, team 1 scores it.
+  // Tile j is first read in phase 2j; every wave waits for its own loads of it
+  // before the barrier that opens that phase.  A wave issues its share of its
+  // next tile in each of its value phases (team 0 tile i+3 in phase 2i+1, team 1
+  // tile i+2 in phase 2i, each into the buffer of a tile finished by then), and
+  // when its next score phase starts a new query token it loads that token's Q
+  // there first.  Prologue: team 0 issues tiles 0..2, team 1 tiles 0..1.
+  {
+    const int t0 = uni(lg.c.t);
+    const int pro = team == 0 ? kNBuf - 1 : kNBuf - 2;
+    for (int k = 0; k < pro && lg.valid; ++k) issue();
+    load_q(t0);
+  }
+  for (int i = 0;; ++i) {
+    const bool has = i < issued;
+    // ---- phase 2i.  Loads complete in issue order: tile i has landed once at
+    // most the loads of the tiles issued after it are outstanding.
+    if (has) wait_vm(nmine * (issued - i - 1));
+    barrier();
+    if (team == 1) {
+      if (has && i > 0 && (desc_of(i) & kFirstOfSeg)) load_q(tok_of(i));
+      if (lg.valid) issue();  // tile i+2
+      if (i > 0) value_phase(i - 1);
+    } else if (has) {
+      score_phase(i);
+    }
+    // ---- phase 2i+1
+    barrier();
+    if (!has) break;
+    if (team == 0) {
+      if (i + 1 < issued && (desc_of(i + 1) & kFirstOfSeg)) load_q(tok_of(i + 1));
+      if (lg.valid) issue();  // tile i+3
+      value_phase(i);
+    } else {
+      score_phase(i);
+    }
+  }
+}
+
+}  // namespace
+
+bool v3_kernels_available() { return true; }
+
+hipError_t launch_decode_v3(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(decode_v4_kernel, dim3(a.plan.G), dim3(512), 0, st, a.plan.q_start,
+                     a.plan.kv_lens, a.block_table, (const uint16_t*)a.pool,
+                     (const uint16_t*)a.q_lat, (uint16_t*)a.o_lat, (uint16_t*)a.ws_o, a.ws_lse,
+                     a.err, a.plan.B, a.plan.T, a.plan.causal, a.plan.G, a.plan.U, a.max_blocks,
+                     a.num_blocks, a.scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -97,11 +97,9 @@ mla_status plan_decode(const mla_config& c, int32_t B, const int32_t* qs, const 
     int cus = 0;
     mla_status s = device_cus(&cus);
     if (s != MLA_OK) return s;
-    // one KV range per compute unit's worth of workgroups, all resident at once:
-    // the V3 kernel runs two workgroups (one per half of the heads) per range and
-    // one workgroup per compute unit (its LDS footprint), the generic kernel one
-    // workgroup per range and group of heads
-    G = (is_v3_bf16(c) && v3_kernels_available()) ? (cus / 2 > 0 ? cus / 2 : 1) : cus;
+    // one KV range per compute unit, all resident at once: the V3 kernel runs
+    // one workgroup per range and (by its LDS footprint) one per compute unit
+    G = cus;
   }
   if (G > U) G = U;
   if (G > (1 << 30)) G = 1 << 30;

@@ -54,6 +54,34 @@ __device__ inline int units_before_seq(const PlanArgs& p, int b_end) {
   return uni(acc);
 }
 
+// True when the device length arrays describe a valid batch whose unit and
+// query-token totals equal the host plan's (U, T): q_start[0] = 0, every
+// sequence has 0 <= q <= L, L >= 1 and ceil(L / block_size) <= max_blocks,
+// q_start[B] = T and the units add up to U.  Every index the kernels derive
+// from the device arrays (token, block-table column, unit, range, partial
+// slot) then stays inside buffers sized from the host copies.  Wave-uniform.
+__device__ inline bool plan_consistent(const PlanArgs& p, int max_blocks) {
+  const int lane = threadIdx.x & 63;
+  int64_t tot = 0;
+  int bad = (ldc(p.q_start, 0) != 0 || ldc(p.q_start, p.B) != p.T) ? 1 : 0;
+  for (int base = 0; base < p.B; base += 64) {
+    const int b = base + lane;
+    int64_t v = 0;
+    if (b < p.B) {
+      const int q = ldc(p.q_start, b + 1) - ldc(p.q_start, b);
+      const int L = ldc(p.kv_lens, b);
+      if (q < 0 || L < 1 || q > L || (L + p.block_size - 1) / p.block_size > max_blocks)
+        bad = 1;
+      else
+        v = seq_units_before(L, q, q, p.block_size, p.causal);
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
+    tot += v;
+  }
+  return __ballot(bad) == 0 && uni((int)(tot == p.U)) != 0;
+}
+
 struct TokenCursor {
   int b;   // sequence
   int j;   // query token index within the sequence

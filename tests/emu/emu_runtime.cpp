@@ -1,7 +1,9 @@
 // Fiber scheduler, wavefront collectives and guarded allocations of the host
 // emulator (see include/emu_runtime.h).  x86-64 Linux only.
+#include <signal.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 #include <sys/mman.h>
 #include <unistd.h>
 
@@ -402,7 +404,49 @@ extern "C" {
 
 // Memory whose end touches an inaccessible page: an access past the last
 // 16-byte granule faults.  The pointer is 16-byte aligned.
+// A fault inside a kernel is almost always an access past a guarded
+// allocation: report the address, the workgroup and work-item, and the
+// allocation it is nearest to, then abort.
+static void emu_segv(int, siginfo_t* si, void*) {
+  char buf[256];
+  const uintptr_t a = (uintptr_t)si->si_addr;
+  int n = snprintf(buf, sizeof buf, "emulator: memory fault at %p (block %u,%u,%u", si->si_addr,
+                   emu::g_bid.x, emu::g_bid.y, emu::g_bid.z);
+  if (emu::g_tid) n += snprintf(buf + n, sizeof buf - n, ", thread %u", emu::g_tid->x);
+  n += snprintf(buf + n, sizeof buf - n, ")\n");
+  if (write(2, buf, n) < 0) {}
+  for (auto& kv : g_allocs) {
+    const uintptr_t lo = (uintptr_t)kv.second.base, hi = lo + kv.second.bytes;
+    if (a >= lo && a < hi) {
+      n = snprintf(buf, sizeof buf, "emulator:   inside the mapping of buffer %p (%zu bytes "
+                   "mapped): offset %ld from the buffer start\n", kv.first, kv.second.bytes,
+                   (long)(a - (uintptr_t)kv.first));
+      if (write(2, buf, n) < 0) {}
+    }
+  }
+  signal(SIGSEGV, SIG_DFL);
+  abort();
+}
+
+static void install_segv_handler() {
+  static bool done = false;
+  if (done) return;
+  done = true;
+  struct sigaction sa;
+  memset(&sa, 0, sizeof sa);
+  sa.sa_sigaction = emu_segv;
+  sa.sa_flags = SA_SIGINFO | SA_ONSTACK;
+  static char alt[1 << 16];
+  stack_t st;
+  st.ss_sp = alt;
+  st.ss_size = sizeof alt;
+  st.ss_flags = 0;
+  sigaltstack(&st, nullptr);
+  sigaction(SIGSEGV, &sa, nullptr);
+}
+
 void* emu_alloc(size_t bytes) {
+  install_segv_handler();
   const size_t kPage = 4096;
   const size_t n = (bytes + 15) & ~(size_t)15;
   const size_t pages = (n + kPage - 1) / kPage;

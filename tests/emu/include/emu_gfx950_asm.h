@@ -27,4 +27,31 @@ __forceinline__ void dma16(const char* base, uint32_t voff, char* lds_dst) {
   ::emu::dma16(base + voff, lds_dst);
 }
 
+inline uint32_t opaque(uint32_t x) { return x; }
+
+// Buffer-resource stores: bounds-checked against the resource's byte size
+// (the hardware drops such a store; in the emulator it is an error, since no
+// kernel here means to rely on that).
+struct buf_t {
+  char* base;
+  uint32_t bytes;
+};
+inline buf_t buf_rsrc(void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  if ((uint32_t)::emu::readfirstlane((unsigned)(b >> 32)) != (uint32_t)(b >> 32) ||
+      (uint32_t)::emu::readfirstlane((unsigned)b) != (uint32_t)b ||
+      (uint32_t)::emu::readfirstlane(bytes) != bytes)
+    ::emu::fail("buffer resource differs between lanes");
+  return buf_t{(char*)base, bytes};
+}
+inline void buf_store_b32(uint32_t v, buf_t r, uint32_t voff, uint32_t soff) {
+  if ((uint64_t)voff + soff + 4 > r.bytes) ::emu::fail("buffer store out of range");
+  memcpy(r.base + voff + soff, &v, 4);
+}
+inline void buf_store_b64(uint32_t lo, uint32_t hi, buf_t r, uint32_t voff, uint32_t soff) {
+  if ((uint64_t)voff + soff + 8 > r.bytes) ::emu::fail("buffer store out of range");
+  memcpy(r.base + voff + soff, &lo, 4);
+  memcpy(r.base + voff + soff + 4, &hi, 4);
+}
+
 }  // namespace mla

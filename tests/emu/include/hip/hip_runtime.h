@@ -123,4 +123,10 @@ inline unsigned long long __ballot(int pred) {
 #define __builtin_amdgcn_permlane32_swap(a, b, fi, bc) ::emu::permlane_swap((a), 32)
 #define __builtin_amdgcn_s_waitcnt(x) ::emu::s_waitcnt(x)
 #define __builtin_amdgcn_sched_barrier(x) ((void)0)
+#define __builtin_amdgcn_sched_group_barrier(m, n, id) ((void)0)
+// hardware transcendentals: the emulator uses the libm functions (the GPU's are
+// within about 1 ulp of them)
+#define __builtin_amdgcn_exp2f(x) exp2f(x)
+#define __builtin_amdgcn_logf(x) log2f(x)
+#define __builtin_amdgcn_rcpf(x) (1.0f / (x))
 #define __builtin_amdgcn_s_setprio(x) ((void)0)
