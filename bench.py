@@ -112,6 +112,29 @@ def cpu_baseline(workload: str, budget_s: float):
                       f"naive fp64 attention, {spent:.1f} s wall"}
 
 
+COPY_BYTES = 1 << 30
+
+
+def profile_decode(st, copies: int, calls: int) -> int:
+    """Kernel launches for hardware-counter runs: a plain device-to-device copy
+    of COPY_BYTES (its FETCH_SIZE / WRITE_SIZE per byte scale the decode
+    kernel's counters to bytes), then `calls` decode calls rotating over the
+    same cache copies as the timed benchmark."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=st.dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for i in range(calls):
+        st.decode(st.pools[i % copies])
+    torch.cuda.synchronize()
+    log(f"[bench] profile mode: 1 copy of {COPY_BYTES} B, {calls} decode calls over {copies} "
+        f"cache copies")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +145,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pool-copies", type=int, default=0,
                     help="cache copies rotated between steps (0: enough for >= 1 GB)")
+    ap.add_argument("--profile-decode", type=int, default=0, metavar="N",
+                    help="counter-run mode: one 1 GiB device copy (the reference kernel for "
+                         "scaling HBM byte counters), then N decode calls over the rotated "
+                         "cache copies, nothing else; prints no JSON line")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -145,6 +172,8 @@ def main() -> int:
         f"x{copies}")
     st = DeviceStep(inp, pool_copies=copies)
     pools = st.pools
+    if args.profile_decode:
+        return profile_decode(st, copies, args.profile_decode)
 
     def step(i, ev=None):
         # ev: events before absorb / after absorb / after append / after decode / after out_proj

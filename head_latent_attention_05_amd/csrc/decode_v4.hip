@@ -153,35 +153,26 @@ struct Loader {
   }
 };
 
-// This wave's direct-to-LDS loads of one tile: latent rows W, W+8, W+16, W+24
-// (one 1 KiB load each) and, for waves 0-3, the RoPE parts of rows 8W..8W+7.
+// This wave's direct-to-LDS loads of one tile: latent rows w, w+8, w+16, w+24
+// (one 1 KiB load each) and, for waves 0-3, the RoPE parts of rows 8w..8w+7.
 // Rows past the end of a partial tile repeat its last valid row (their scores
-// are masked; repeating keeps every value finite).
-template <int W>
-__device__ __forceinline__ void issue_rows(const char* blk, int last, char* buf, int lane) {
+// are masked; repeating keeps every value finite).  All latent rows of a wave
+// share one chunk swizzle (fa(w + 8r) = fa(w)), so one lane offset serves them;
+// the RoPE offset is formed here from the lane id, at issue time, rather than
+// kept in a register.
+__device__ __forceinline__ void issue_rows(int wave, const char* blk, int last, char* buf,
+                                           uint32_t lane) {
+  const uint32_t lat_off = (lane ^ (uint32_t)fa(wave)) << 4;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int i = W + 8 * r;
-    dma16(blk + min(i, last) * kRowBytes, (uint32_t)((lane ^ fa(i)) << 4), buf + i * kLatBytes);
+    const int i = wave + 8 * r;
+    dma16(blk + min(i, last) * kRowBytes, lat_off, buf + i * kLatBytes);
   }
-  if (W < 4) {
-    const int t = 8 * W + (lane >> 3);
-    const uint32_t voff = min(t, last) * kRowBytes + kLatBytes + (((lane & 7) ^ fb(t)) << 4);
-    dma16(blk, voff, buf + kRegionB + W * 1024);
-  }
-}
-
-__device__ __forceinline__ void issue_rows_w(int wave, const char* blk, int last, char* buf,
-                                             int lane) {
-  switch (wave) {
-    case 0: issue_rows<0>(blk, last, buf, lane); break;
-    case 1: issue_rows<1>(blk, last, buf, lane); break;
-    case 2: issue_rows<2>(blk, last, buf, lane); break;
-    case 3: issue_rows<3>(blk, last, buf, lane); break;
-    case 4: issue_rows<4>(blk, last, buf, lane); break;
-    case 5: issue_rows<5>(blk, last, buf, lane); break;
-    case 6: issue_rows<6>(blk, last, buf, lane); break;
-    default: issue_rows<7>(blk, last, buf, lane); break;
+  if (wave < 4) {
+    const int t = 8 * wave + (int)(lane >> 3);
+    const uint32_t voff =
+        (uint32_t)(min(t, last) * kRowBytes + kLatBytes) + (((lane & 7) ^ (uint32_t)fb(t)) << 4);
+    dma16(blk, voff, buf + kRegionB + wave * 1024);
   }
 }
 
@@ -198,6 +189,34 @@ __device__ __forceinline__ float head_sum(float x) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+
+// Per-lane geometry of the MFMA operands (lane = 16 g4 + l16).  Tile buffers
+// are 4 KiB aligned in the shared block and the chunk swizzles only touch
+// offset bits 4..7, so every operand address is (tile base + lane part) ^ (a
+// constant selecting the chunk):
+//   score reads (A operand = K rows): row l16 (+16 rows for the second token
+//   block), latent chunk 4kk + g4 -> (lat ^ ((kk & 3) << 6)) + 256 (kk >> 2),
+//   RoPE chunk 4r + g4 (kk = 16 + r) -> rope ^ (r << 6);
+//   transposing reads (A operand = V^T) of feature block 8wk + f: rows
+//   4g4 + (l16 >> 2) (+16), features 16(8wk + f) + 4(l16 & 3), i.e. chunk
+//   16wk + 2f + ((l16 >> 1) & 1) -> val ^ (f << 5).
+struct LaneGeom {
+  int lane, l16, g4;
+  __device__ __forceinline__ explicit LaneGeom(uint32_t tid)
+      : lane((int)(tid & 63)), l16((int)(tid & 15)), g4((int)((tid >> 4) & 3)) {}
+  __device__ __forceinline__ uint32_t lat() const {
+    const int f = fa(l16);
+    return l16 * kLatBytes + (((f >> 2) & 3) << 6) + ((g4 ^ (f & 2)) << 4);
+  }
+  __device__ __forceinline__ uint32_t rope() const {
+    return kRegionB + l16 * kRopeBytes + ((g4 ^ fb(l16)) << 4);
+  }
+  __device__ __forceinline__ uint32_t val(int wk) const {
+    const int trow = 4 * g4 + (l16 >> 2);
+    return trow * kLatBytes + ((fa(trow) >> 1) << 5) + (((l16 >> 1) & 1) << 4) + 8 * (l16 & 1) +
+           wk * 256;
+  }
+};
 
 struct Shared {
   char tiles[kNBuf][kTileBytes];
@@ -237,35 +256,17 @@ __global__ __launch_bounds__(512, 1) void decode_v4_kernel(
   const int u0 = (int)range_start(w, U, G), u1 = (int)range_start(w + 1, U, G);
   if (u0 >= u1) return;
 
-  const int l16 = lane & 15;  // MFMA column (head) / row index
-  const int g4 = lane >> 4;   // 16-lane group
-  const int shead = 64 * team + 16 * wk + l16;  // head this lane scores
-
-  // LDS addresses, as byte offsets from the start of the shared block.  Tile
-  // buffers are 4 KiB aligned there and the swizzles only touch offset bits
-  // 4..7, so an offset is (tile base + per-lane part) ^ (a constant selecting
-  // the chunk): no per-chunk offsets are kept in registers.
+  // LDS addresses are byte offsets from the start of the shared block (see
+  // LaneGeom); the lane-dependent parts are rebuilt inside each phase from the
+  // lane id instead of being held in registers across the tile loop.
   const char* lds0 = (const char*)&sh;
-  //   score reads (A operand = K rows): row l16 (+16 rows for the second token
-  //   block), latent chunk 4kk + g4 -> (lat_lane ^ ((kk & 3) << 6)) + 256 (kk >> 2),
-  //   RoPE chunk 4r + g4 (kk = 16 + r) -> rope_lane ^ (r << 6);
-  //   transposing reads (A operand = V^T) of feature block 8wk + f: rows
-  //   4g4 + (l16 >> 2) (+16), features 16(8wk + f) + 4(l16 & 3), i.e. chunk
-  //   16wk + 2f + ((l16 >> 1) & 1) -> val_lane ^ (f << 5).
-  const int faL = fa(l16), fbL = fb(l16);
-  const int lat_lane = l16 * kLatBytes + (((faL >> 2) & 3) << 6) + ((g4 ^ (faL & 2)) << 4);
-  const int rope_lane = kRegionB + l16 * kRopeBytes + ((g4 ^ fbL) << 4);
-  const int trow = 4 * g4 + (l16 >> 2);
-  const int val_lane = trow * kLatBytes + ((fa(trow) >> 1) << 5) + (((l16 >> 1) & 1) << 4) +
-                       8 * (l16 & 1) + wk * 256;
-  // global offsets (bytes) of this lane: query row of head shead, columns 8g4..
-  const int q_lane = (shead * kRow + 8 * g4) * 2;
 
   const char* pool_b = (const char*)pool;
   const int nmine = wave < 4 ? 5 : 4;  // direct-to-LDS loads per tile of this wave
   Loader lg;
   lg.init(p, block_table, max_blocks, u0, u1);
   int issued = 0;  // tiles this wave has issued
+  bool pending_adv = false;  // the walk still describes the tile last issued
 
   u32x4 qreg[18];
   f32x4 acc[8][4];  // [feature block][head block]
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(512, 1) void decode_v4_kernel(
     const int bad_ = uni(lg.blk_raw < 0 || lg.blk_raw >= num_blocks);
     const int phys_ = uni(bad_ ? 0 : lg.blk_raw);
     const char* blk_ = pool_b + ((int64_t)phys_ * kBS + lg.half * kTile) * kRowBytes;
-    issue_rows_w(wave, blk_, bad_ ? 0 : lg.nvalid - 1, sh.tiles[k_], lane);
+    issue_rows(wave, blk_, bad_ ? 0 : lg.nvalid - 1, sh.tiles[k_], opaque(threadIdx.x) & 63);
     if (lane == 0) {
       sh.desc[wave][k_][0] = (bad_ ? 0 : lg.nvalid) | (lg.first ? kFirstOfSeg : 0) |
                              (lg.last_of_segment() ? kLastOfSeg : 0) |
@@ -284,8 +285,20 @@ __global__ __launch_bounds__(512, 1) void decode_v4_kernel(
                              (lg.nseg > 0 ? kSecondSlot : 0);
       sh.desc[wave][k_][1] = lg.c.t;
     }
-    lg.next(p, block_table, max_blocks);
     ++issued;
+    pending_adv = true;
+  };
+  // Moves the walk to the next tile.  Its scalar loads (block table, lengths)
+  // share a wait counter with LDS reads and may return out of order, so while
+  // one is outstanding every LDS wait the compiler emits must be a full one;
+  // waiting for them here, at the end of the short score phase, keeps the LDS
+  // reads of the other phases pipelined.
+  auto advance = [&]() {
+    if (pending_adv) {
+      lg.next(p, block_table, max_blocks);
+      pending_adv = false;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   };
   auto desc_of = [&](int i) { return uni(sh.desc[wave][i % kNBuf][0]); };
   auto tok_of = [&](int i) { return uni(sh.desc[wave][i % kNBuf][1]); };
@@ -294,24 +307,27 @@ __global__ __launch_bounds__(512, 1) void decode_v4_kernel(
   // order); it sits right here so the compiler knows no load into qreg is
   // pending anywhere else and adds no waits of its own inside the tile loop.
   auto load_q = [&](int tok) {
-    const char* qb = (const char*)qlat + (int64_t)tok * (kH * kRow * 2) + opaque(q_lane);
+    const LaneGeom lg_(opaque(threadIdx.x));
+    const uint32_t q_lane = ((64 * team + 16 * wk + lg_.l16) * kRow + 8 * lg_.g4) * 2;
+    const char* qb = (const char*)qlat + (int64_t)tok * (kH * kRow * 2) + q_lane;
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) qreg[kk] = *(const u32x4*)(qb + 64 * kk);
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
   };
 
   // ---------------------------------------------------------------- S phase
-  auto score_phase = [&](int i) {
-    const int d = desc_of(i);
+  auto score_phase = [&](int i, int d) {
     const char* tb = sh.tiles[i % kNBuf];
+    const LaneGeom lgm(opaque(threadIdx.x));
+    const int lane = lgm.lane, l16 = lgm.l16, g4 = lgm.g4;
     if (d & kFirstOfSeg) {
       m_run = -INFINITY;
       l_part = 0.f;
     }
     f32x4 s0 = {}, s1 = {};
-    u32x4 ka[2][2];  // K operands of k-steps kk and kk+1
-    const uint32_t la = opaque((uint32_t)(tb - lds0) + lat_lane);
-    const uint32_t ra = opaque((uint32_t)(tb - lds0) + rope_lane);
+    u32x4 ka[3][2];  // K operands of k-steps kk .. kk+2
+    const uint32_t la = (uint32_t)(tb - lds0) + lgm.lat();
+    const uint32_t ra = (uint32_t)(tb - lds0) + lgm.rope();
     auto ld = [&](int kk, u32x4* dst) {
       const uint32_t a = kk < 16 ? (la ^ ((kk & 3) << 6)) + (kk >> 2) * 256 : ra ^ ((kk - 16) << 6);
       const int second = kk < 16 ? 16 * kLatBytes : 16 * kRopeBytes;
@@ -319,15 +335,25 @@ __global__ __launch_bounds__(512, 1) void decode_v4_kernel(
       dst[1] = *(const u32x4*)(lds0 + a + second);
     };
     ld(0, ka[0]);
+    ld(1, ka[1]);
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) {
-      if (kk + 1 < 18) ld(kk + 1, ka[(kk + 1) & 1]);
+      if (kk + 2 < 18) ld(kk + 2, ka[(kk + 2) % 3]);
       const bf16x8 qb = __builtin_bit_cast(bf16x8, qreg[kk]);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kk & 1][0]), qb,
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kk % 3][0]), qb,
                                                    s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kk & 1][1]), qb,
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kk % 3][1]), qb,
                                                    s1, 0, 0, 0);
     }
+    // keep the K reads two k-steps ahead of the MFMAs that consume them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads (k-steps 0, 1)
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs (k-step kk)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads (k-step kk+2)
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
     // online softmax: lane holds head l16, tokens 4g4+r (s0) and 16+4g4+r (s1).
     // Weights are 2^(s*scale*log2(e) - m) on the hardware exp2 (v_exp_f32, ~1 ulp;
     // arguments below -126 flush to 0, which is below bf16 resolution of P anyway).
@@ -377,53 +403,73 @@ __global__ __launch_bounds__(512, 1) void decode_v4_kernel(
   };
 
   // ---------------------------------------------------------------- P phase
-  auto value_phase = [&](int i) {
-    const int d = desc_of(i);
+  auto value_phase = [&](int i, int d, int tok) {
     const char* tb = sh.tiles[i % kNBuf];
-    if (d & kFirstOfSeg) {
+    const LaneGeom lgm(opaque(threadIdx.x));
+    const int lane = lgm.lane, l16 = lgm.l16, g4 = lgm.g4;
+    // LDS reads first: the rescale factors of the team's heads (the decision
+    // to rescale waits for them alone), the P^T fragments, and the V^T operands
+    // of feature blocks 0..2, all in flight together; the loop below keeps
+    // three feature blocks ahead (the transposing read's latency is several
+    // MFMAs long).
+    const f32x4 al = {sh.alpha[team][0][l16], sh.alpha[team][1][l16], sh.alpha[team][2][l16],
+                      sh.alpha[team][3][l16]};
+    bf16x8 pb[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.pbuf[team][h][lane]);
+    const bool first = (d & kFirstOfSeg) != 0;
+    const bool resc =
+        !first && __ballot((al[0] != 1.f) | (al[1] != 1.f) | (al[2] != 1.f) | (al[3] != 1.f)) != 0;
+    const uint32_t va0 = (uint32_t)(tb - lds0) + lgm.val(wk);
+    i16x4 vr[4][2];
+    auto ldv = [&](int f, i16x4* dst) {
+      const char* vp = lds0 + (va0 ^ (f << 5));
+      dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)vp);
+      dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + 16 * kLatBytes));
+    };
+    ldv(0, vr[0]);
+    ldv(1, vr[1]);
+    ldv(2, vr[2]);
+    if (first) {
 #pragma unroll
       for (int f = 0; f < 8; ++f)
 #pragma unroll
         for (int h = 0; h < 4; ++h) acc[f][h] = f32x4{};
-    } else {
-      const f32x4 al = {sh.alpha[team][0][l16], sh.alpha[team][1][l16], sh.alpha[team][2][l16],
-                        sh.alpha[team][3][l16]};
-      const bool resc = (al[0] != 1.f) | (al[1] != 1.f) | (al[2] != 1.f) | (al[3] != 1.f);
-      if (__ballot(resc) != 0) {
+    } else if (resc) {
 #pragma unroll
-        for (int f = 0; f < 8; ++f)
+      for (int f = 0; f < 8; ++f)
 #pragma unroll
-          for (int h = 0; h < 4; ++h) acc[f][h] *= al[h];
-      }
+        for (int h = 0; h < 4; ++h) acc[f][h] *= al[h];
     }
-    bf16x8 pb[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.pbuf[team][h][lane]);
-    const uint32_t va0 = opaque((uint32_t)(tb - lds0) + val_lane);
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-      const char* vp = lds0 + (va0 ^ (f << 5));
-      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)vp);
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + 16 * kLatBytes));
-      const bf16x8 va =
-          __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      if (f + 3 < 8) ldv(f + 3, vr[(f + 3) & 3]);
+      const bf16x8 va = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(vr[f & 3][0], vr[f & 3][1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int h = 0; h < 4; ++h)
         acc[f][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[h], acc[f][h], 0, 0, 0);
     }
+    // keep the reads three blocks ahead of the MFMAs that consume them
+#pragma unroll
+    for (int f = 0; f < 5; ++f) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 LDS reads (block f+3)
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // 4 MFMAs (block f)
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
     if (d & kLastOfSeg) {
       const f32x4 inv = {sh.invl[team][0][l16], sh.invl[team][1][l16], sh.invl[team][2][l16],
                          sh.invl[team][3][l16]};
       uint16_t* base;
       if (d & kWhole) {
-        base = o_lat + (int64_t)tok_of(i) * kH * kDC;
+        base = o_lat + (int64_t)tok * kH * kDC;
       } else {
         const int slot = 2 * w + ((d & kSecondSlot) ? 1 : 0);
         base = ws_o + (int64_t)uni(slot) * kH * kDC;
       }
       // lane holds features 16(8wk+f) + 4g4 + r of head 64team + 16h + l16
       const buf_t out = buf_rsrc(base, kH * kDC * 2);
-      const uint32_t voff = opaque(((64 * team + l16) * kDC + 128 * wk + 4 * g4) * 2);
+      const uint32_t voff = ((64 * team + l16) * kDC + 128 * wk + 4 * g4) * 2;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
 #pragma unroll
@@ -447,32 +493,47 @@ __global__ __launch_bounds__(512, 1) void decode_v4_kernel(
   {
     const int t0 = uni(lg.c.t);
     const int pro = team == 0 ? kNBuf - 1 : kNBuf - 2;
-    for (int k = 0; k < pro && lg.valid; ++k) issue();
+    for (int k = 0; k < pro && lg.valid; ++k) {
+      issue();
+      advance();
+    }
     load_q(t0);
+    // no scalar load may look outstanding at the loop entry (the compiler
+    // would otherwise make every LDS wait in the loop a full one)
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   }
+  // Tile descriptors are read before the barrier that opens a phase (the wave
+  // waits there anyway), so no LDS read is outstanding when a phase starts.
+  int d_prev = 0, t_prev = 0;  // descriptor and token of tile i-1
   for (int i = 0;; ++i) {
     const bool has = i < issued;
+    const int d_i = has ? desc_of(i) : 0, t_i = has ? tok_of(i) : 0;
     // ---- phase 2i.  Loads complete in issue order: tile i has landed once at
     // most the loads of the tiles issued after it are outstanding.
     if (has) wait_vm(nmine * (issued - i - 1));
     barrier();
     if (team == 1) {
-      if (has && i > 0 && (desc_of(i) & kFirstOfSeg)) load_q(tok_of(i));
+      if (has && i > 0 && (d_i & kFirstOfSeg)) load_q(t_i);
       if (lg.valid) issue();  // tile i+2
-      if (i > 0) value_phase(i - 1);
+      if (i > 0) value_phase(i - 1, d_prev, t_prev);
     } else if (has) {
-      score_phase(i);
+      score_phase(i, d_i);
+      advance();
     }
     // ---- phase 2i+1
+    const int d_next = i + 1 < issued ? desc_of(i + 1) : 0;
     barrier();
     if (!has) break;
     if (team == 0) {
-      if (i + 1 < issued && (desc_of(i + 1) & kFirstOfSeg)) load_q(tok_of(i + 1));
+      if (i + 1 < issued && (d_next & kFirstOfSeg)) load_q(tok_of(i + 1));
       if (lg.valid) issue();  // tile i+3
-      value_phase(i);
+      value_phase(i, d_i, t_i);
     } else {
-      score_phase(i);
+      score_phase(i, d_i);
+      advance();
     }
+    d_prev = d_i;
+    t_prev = t_i;
   }
 }
 

@@ -29,15 +29,15 @@ FLAGS = [
 ]
 
 
-def _sources():
-    hips = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def _sources(csrc: str = CSRC):
+    hips = sorted(glob.glob(os.path.join(csrc, "*.hip")))
     return hips, [os.path.join(HERE, "emu_runtime.cpp")]
 
 
-def _stamp() -> str:
+def _stamp(csrc: str = CSRC) -> str:
     h = hashlib.sha256()
-    hips, cpps = _sources()
-    deps = hips + cpps + sorted(glob.glob(os.path.join(CSRC, "*.h")))
+    hips, cpps = _sources(csrc)
+    deps = hips + cpps + sorted(glob.glob(os.path.join(csrc, "*.h")))
     deps += sorted(glob.glob(os.path.join(HERE, "include", "**", "*.h"), recursive=True))
     deps += [os.path.join(ROOT, "include", "mla.h"), os.path.abspath(__file__)]
     for p in deps:
@@ -49,8 +49,8 @@ def _stamp() -> str:
 
 
 def _compile(args):
-    src, is_hip = args
-    obj = os.path.join(OUT_DIR, os.path.basename(src) + ".emu.o")
+    src, is_hip, out_dir = args
+    obj = os.path.join(out_dir, os.path.basename(src) + ".emu.o")
     cmd = [CXX, *FLAGS]
     if is_hip:
         cmd += ["-x", "c++", "-include", "emu_gfx950_asm.h"]
@@ -61,27 +61,35 @@ def _compile(args):
     return obj
 
 
-def build(force: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    stamp = _stamp()
-    stamp_file = os.path.join(OUT_DIR, "stamp")
-    if not force and os.path.exists(LIB) and os.path.exists(stamp_file):
-        with open(stamp_file) as f:
-            if f.read() == stamp:
-                return LIB
-    hips, cpps = _sources()
-    jobs = [(s, True) for s in hips] + [(s, False) for s in cpps]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        objs = list(ex.map(_compile, jobs))
-    tmp = LIB + ".tmp"
-    r = subprocess.run([CXX, "-shared", "-fPIC", "-o", tmp, *objs], capture_output=True,
-                       text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"emulator link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    with open(stamp_file, "w") as f:
-        f.write(stamp)
-    return LIB
+def build(force: bool = False, csrc: str = CSRC, out_dir: str = OUT_DIR) -> str:
+    """Build the emulated library from the kernel sources in `csrc` (default:
+    the library's own) into `out_dir`; rebuilt only when a source changed.
+    Concurrent builds (parallel test workers) serialise on a lock file."""
+    import fcntl
+
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "libmla_emu.so")
+    with open(os.path.join(out_dir, "lock"), "w") as lock:
+        fcntl.flock(lock, fcntl.LOCK_EX)
+        stamp = _stamp(csrc)
+        stamp_file = os.path.join(out_dir, "stamp")
+        if not force and os.path.exists(lib) and os.path.exists(stamp_file):
+            with open(stamp_file) as f:
+                if f.read() == stamp:
+                    return lib
+        hips, cpps = _sources(csrc)
+        jobs = [(s, True, out_dir) for s in hips] + [(s, False, out_dir) for s in cpps]
+        with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+            objs = list(ex.map(_compile, jobs))
+        tmp = lib + ".tmp"
+        r = subprocess.run([CXX, "-shared", "-fPIC", "-o", tmp, *objs], capture_output=True,
+                           text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"emulator link failed:\n{r.stderr}")
+        os.replace(tmp, lib)
+        with open(stamp_file, "w") as f:
+            f.write(stamp)
+    return lib
 
 
 if __name__ == "__main__":

@@ -19,8 +19,8 @@ SENTINEL_F32 = 0x7FC00001
 
 
 class Emu:
-    def __init__(self, cus: int = 8, seed: int = 1):
-        lib = ctypes.CDLL(build_emu.build())
+    def __init__(self, cus: int = 8, seed: int = 1, lib_path: Optional[str] = None):
+        lib = ctypes.CDLL(lib_path or build_emu.build())
         B.declare(lib)
         lib.emu_alloc.restype = ctypes.c_void_p
         lib.emu_alloc.argtypes = [ctypes.c_size_t]

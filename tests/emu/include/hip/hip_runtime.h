@@ -130,3 +130,9 @@ inline unsigned long long __ballot(int pred) {
 #define __builtin_amdgcn_logf(x) log2f(x)
 #define __builtin_amdgcn_rcpf(x) (1.0f / (x))
 #define __builtin_amdgcn_s_setprio(x) ((void)0)
+// shader clock: a counter that only moves forward
+inline unsigned long long emu_clock_() {
+  static unsigned long long t = 0;
+  return t += 4;
+}
+#define __builtin_amdgcn_s_memtime() emu_clock_()
