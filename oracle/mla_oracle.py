@@ -26,8 +26,12 @@ a cached key is computed in fp32 as ``x*cos - x2*sin`` / ``x2*cos + x*sin``
 with every product and sum rounded to fp32 (no fused multiply-add) and then
 rounded to bf16 (nearest-even) for bf16 caches.
 
-Every function here is pinned by tests (closed forms, brute force, special
-cases, the absorption identity); none is "parity unpinned".
+Every function here is pinned by tests/test_oracle_pins.py against something
+other than itself: closed forms of the RoPE table and rotation, brute-force
+scalar loops, torch's scaled-dot-product attention, special cases, the
+absorption identity, and, for the cache rows written by append_cache, an exact
+fp64 rotation at each token's true position read back through the paged pool
+plus the relative-position property of the scores; none is "parity unpinned".
 """
 from __future__ import annotations
 

@@ -158,6 +158,61 @@ def test_append_gather_roundtrip_and_sentinels():
     assert np.all(raw[untouched] == 0x7FC00001)
 
 
+def _bf16_ulp(x):
+    """Spacing of bf16 values at |x| (8 significant bits)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("workload,lens", [("tiny", [200, 5, 129, 64]),
+                                           ("batch64", [300, 65, 130])])
+def test_pool_rope_columns_rotate_at_the_true_position(workload, lens):
+    """The RoPE part of every cached row is k_pe rotated at its token's own
+    position ([MLA explainer] RoPE module; forward_inference_absorbed caches the
+    rotated k_r), checked against an exact fp64 rotation through the paged pool
+    (shuffled block table, positions across block boundaries): within the
+    storage rounding for every position, and exact at position 0."""
+    inp = synth.make_inputs(workload, kv_lens=lens, q_len=1)
+    d = inp.dims
+    pool = O.build_pool(inp)
+    dc = d.d_latent
+    for b, L in enumerate(inp.kv_lens):
+        L = int(L)
+        rows = O.gather_rows(pool, d, 64, inp.block_table, b, L)
+        kpe = O.storage_to_f64(inp.k_pe[b], d.dtype)
+        exact = O.rope_f64(kpe, np.arange(L), d.d_rope)
+        got = rows[:, dc:]
+        if d.dtype == "bf16":
+            # fp32 rotation then one bf16 rounding: at most one bf16 ulp away
+            bound = _bf16_ulp(exact) + 1e-30
+        else:
+            # fp32 products and sums: a few fp32 ulps of the operand magnitude
+            h = d.d_rope // 2
+            mag = np.concatenate([np.abs(kpe[:, :h]) + np.abs(kpe[:, h:])] * 2, axis=1)
+            bound = 4 * 2.0 ** -24 * mag + 1e-30
+        assert np.all(np.abs(got - exact) <= bound), (b, np.argwhere(np.abs(got - exact) > bound)[:4])
+        np.testing.assert_array_equal(got[0], kpe[0])  # position 0 is the identity
+
+
+def test_pool_rope_scores_depend_only_on_relative_position():
+    """Through the pool, a query rotated at position m scores a key cached at
+    position n by a function of m - n alone (RoPE's defining property): every
+    cached key is the same vector, so scores along a diagonal must agree."""
+    inp = synth.make_inputs("tiny", kv_lens=[256], q_len=1)
+    d = inp.dims
+    key = np.random.default_rng(7).standard_normal(d.d_rope).astype(np.float32)
+    inp.k_pe[0][:] = key
+    pool = O.build_pool(inp)
+    rows = O.gather_rows(pool, d, 64, inp.block_table, 0, 256)[:, d.d_latent:]
+    q = np.random.default_rng(8).standard_normal(d.d_rope)
+    score = lambda m, n: float(O.rope_f64(q, m, d.d_rope) @ rows[n])
+    for delta in (0, 1, 17, 64, 100):
+        vals = [score(n + delta, n) for n in (0, 3, 63, 64, 65, 130, 255 - delta)]
+        np.testing.assert_allclose(vals, vals[0], rtol=0, atol=1e-5)
+    # and it is not constant in the difference (a dropped rotation would be)
+    assert abs(score(5, 0) - score(0, 0)) > 1e-3
+
+
 def test_paging_is_placement_only():
     """Another block permutation changes where rows live, not what they hold."""
     inp = synth.make_inputs("tiny", kv_lens=[130, 64], q_len=1)
