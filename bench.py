@@ -6,8 +6,10 @@ Prints ONE JSON line on stdout.  ``value`` = cached-token reads per second over
 the whole step (one read = one 576-value latent row consumed by all 128 heads of
 one query token), inputs resident in HBM.  The ``roofline`` object covers the
 decode call (the dominant kernel) with its algorithmic bytes, timed live with
-HIP events on the library's stream; ``cpu_baseline`` times the CPU oracle on a
-bounded sample of the same workload.
+HIP events on the library's stream, against the HBM peak and against a 1 GiB
+device copy timed in the same run; ``workloads`` gives the decode call alone on
+the other workloads; ``cpu_baseline`` times the CPU oracle on a bounded sample
+of the step's own inputs.
 
     python bench.py [--steps K] [--warmup W] [--workload batch64]
 """
@@ -69,47 +71,155 @@ def traffic_from_counters(workload: str):
         return None
 
 
-def cpu_baseline(workload: str, budget_s: float):
-    """The oracle (cache append + naive explicit-decompression attention, fp64)
-    on the first sequences of the workload, 16 heads at a time, until ~budget_s
-    of CPU work.  Reads done are counted per head: one cached-token read is one
-    row consumed by all heads, so k of H heads count k/H of it."""
+def host_info():
+    """Cores this process may run on and the CPU model name."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The oracle on the step's own inputs: with the history rows already in
+    its cache (set-up, untimed, as on the GPU), it appends each sequence's new
+    tokens and runs the naive explicit-decompression attention (fp64, up to the
+    step's output) for that sequence, 16 heads at a time, until ~budget_s of
+    CPU work.  Reads done are counted per head: one cached-token read is one row
+    consumed by all heads, so k of H heads count k/H of it."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
-    from head_latent_attention_05_amd import synth
     from oracle import mla_oracle as O
 
-    full = synth.make_inputs(workload)
-    wl, d = full.workload, full.dims
+    wl, d = inp.workload, inp.dims
     H = d.num_heads
-    lens = [int(x) for x in full.kv_lens]
+    cos32, sin32 = O.rope_table_f32(inp.max_pos(), d.d_rope)
+    pool = O.build_pool(inp, 64, cos32, sin32, which="history")
+    seqs, pos, ck, kp = inp.new_tokens()
     reads, spent, nseq, nheads = 0.0, 0.0, 0, 0
-    for b, L in enumerate(lens):
-        inp = synth.make_inputs(wl, kv_lens=[L], seed=1000 + b)
+    for b in range(len(inp.kv_lens)):
+        a0, a1 = int(inp.q_start[b]), int(inp.q_start[b + 1])
         t0 = time.perf_counter()
-        pool = O.build_pool(inp, 64)
+        O.append_cache(pool, d, 64, seqs[a0:a1], pos[a0:a1], ck[a0:a1], kp[a0:a1],
+                       inp.block_table, cos32, sin32)
         spent += time.perf_counter() - t0
-        rows = lambda i: O.gather_rows(pool, d, 64, inp.block_table, i, int(inp.kv_lens[i]))
+        L = int(inp.kv_lens[b])
+        rows = lambda i, b=b, L=L: O.gather_rows(pool, d, 64, inp.block_table, b, L)
+        q_start = np.array([0, a1 - a0], np.int64)
         nseq += 1
         for h0 in range(0, H, 16):
             heads = list(range(h0, min(H, h0 + 16)))
             t0 = time.perf_counter()
-            O.naive_mla(d, inp.w_uk, inp.w_uv, inp.q_nope, inp.q_pe, rows, inp.kv_lens,
-                        inp.q_start, wl.causal, heads)
+            O.naive_mla(d, inp.w_uk, inp.w_uv, inp.q_nope[a0:a1], inp.q_pe[a0:a1], rows,
+                        np.array([L]), q_start, wl.causal, heads)
             spent += time.perf_counter() - t0
-            reads += kv_reads(inp) * len(heads) / H
+            q = a1 - a0
+            r = sum(L - q + j + 1 for j in range(q)) if wl.causal else q * L
+            reads += r * len(heads) / H
             nheads += len(heads)
             if spent >= budget_s:
                 break
         if spent >= budget_s:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": reads / spent, "unit": "cached-token reads/s", "cores": int(threads),
+    host_cores, model = host_info()
+    blas = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    lens = [int(x) for x in inp.kv_lens[:nseq]]
+    return {"value": reads / spent, "unit": "cached-token reads/s",
+            "cores": int(min(blas, host_cores)), "host_cores": host_cores, "cpu_model": model,
             "kind": "oracle",
-            "sample": f"{nseq} of {len(lens)} sequences of '{workload}' (kv_len {lens[:nseq]}), "
-                      f"{nheads} of their {nseq * H} (sequence, head) pairs, cache append + "
-                      f"naive fp64 attention, {spent:.1f} s wall"}
+            "sample": f"the timed step's own inputs: sequences 0..{nseq - 1} of "
+                      f"{len(inp.kv_lens)} of '{wl.name}' (kv_len {lens}), {nheads} of their "
+                      f"{nseq * H} (sequence, head) pairs; new-token cache append + naive fp64 "
+                      f"attention to the step output, {spent:.1f} s wall"}
+
+
+def copy_bandwidth(dev, nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Device-to-device copy of nbytes (bytes read + bytes written) / time, in
+    GB/s: the achievable streaming rate on this device, measured now."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def decode_bytes_flops(inp):
+    """Algorithmic bytes and flops of one decode call: every attended row read
+    once per query token, q_lat read and o_lat written once; 2 flops per
+    multiply-add over the 576-wide scores and the 512-wide values."""
+    d = inp.dims
+    esz = 2 if d.dtype == "bf16" else 4
+    reads = kv_reads(inp)
+    nbytes = reads * d.row * esz + inp.T * d.num_heads * (d.row + d.d_latent) * esz
+    flops = reads * 2 * d.num_heads * (d.row + d.d_latent)
+    return reads, nbytes, flops
+
+
+def pool_copies_for(st, min_bytes: int = 1 << 30, cap: int = 256):
+    """The step's cache plus clones of it, together at least min_bytes (so
+    rotating over them keeps the working set far above the 256 MB Infinity
+    Cache), at most cap copies."""
+    nb = st.pool.numel() * st.pool.element_size()
+    n = max(1, min(cap, -(-min_bytes // nb)))
+    return [st.pool] + [st.pool.clone() for _ in range(n - 1)]
+
+
+def decode_only(workload: str, calls: int, warmup: int, copy_gbs: float):
+    """Decode-call time alone on another workload (same launch configuration as
+    the headline step), over rotated cache copies."""
+    import numpy as np
+    import torch
+
+    from head_latent_attention_05_amd import synth
+    from head_latent_attention_05_amd.step import DeviceStep
+
+    inp = synth.make_inputs(workload)
+    st = DeviceStep(inp)
+    st.absorb()
+    st.append()
+    pools = pool_copies_for(st)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        st.decode(pools[i % len(pools)])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        st.decode(pools[i % len(pools)])
+        b.record()
+    torch.cuda.synchronize()
+    assert int(st.dev_error.item()) == 0
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg = float(np.mean(ms))
+    reads, nbytes, flops = decode_bytes_flops(inp)
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    tfs = flops / (avg * 1e-3) / 1e12
+    rec = {"decode_us": avg * 1e3, "p50_us": float(np.median(ms)) * 1e3, "calls": calls,
+           "kv_reads": reads, "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+           "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "copy_frac": gbs / copy_gbs,
+           "mfma_tfs": tfs, "mfma_frac": tfs / MFMA_BF16_PEAK_TFS,
+           "bound": "mfma" if inp.workload.causal and inp.T > len(inp.kv_lens) else "hbm",
+           "cache_copies_rotated": len(pools)}
+    del st, pools
+    torch.cuda.empty_cache()
+    return rec
 
 
 COPY_BYTES = 1 << 30
@@ -135,6 +245,67 @@ def profile_decode(st, copies: int, calls: int) -> int:
     return 0
 
 
+def _short_kernel(name: str) -> str:
+    for pre in ("void ", "mla::(anonymous namespace)::"):
+        name = name.replace(pre, "")
+    return name.split("(")[0]
+
+
+def read_counter_runs(dirs):
+    """Mean value per dispatch of every (kernel, counter) in rocprofv3 --pmc CSV
+    output directories; also the dispatch counts."""
+    import csv
+    import collections
+    vals = collections.defaultdict(list)
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    vals[(_short_kernel(r["Kernel_Name"]), r["Counter_Name"])].append(
+                        float(r["Counter_Value"]))
+    return vals
+
+
+DECODE_KERNELS = ("decode_v4_kernel", "merge_v3_kernel")
+
+
+def counters_json(workload: str, dirs, out: str) -> int:
+    """From --pmc runs of `bench.py --profile-decode N` (FETCH_SIZE and
+    WRITE_SIZE each in its own run): the 1 GiB copy's counters give KiB -> byte
+    factors; the decode call's HBM bytes per launch are its kernels' scaled
+    FETCH_SIZE + WRITE_SIZE.  Merged into `out`, keyed by workload and stamped
+    with the kernel-source hash (bench.py ignores it once the sources change)."""
+    vals = read_counter_runs(dirs)
+    copy = [v for (k, c), v in vals.items() if "copyBuffer" in k and c == "FETCH_SIZE"]
+    copyw = [v for (k, c), v in vals.items() if "copyBuffer" in k and c == "WRITE_SIZE"]
+    if not copy or not copyw:
+        log("no copy-kernel FETCH_SIZE / WRITE_SIZE found")
+        return 1
+    ff = COPY_BYTES / (max(max(v) for v in copy) * 1024)
+    wf = COPY_BYTES / (max(max(v) for v in copyw) * 1024)
+    per = {}
+    for k in DECODE_KERNELS:
+        fv, wv = vals.get((k, "FETCH_SIZE")), vals.get((k, "WRITE_SIZE"))
+        if fv and wv:
+            per[k] = {"fetch_bytes": sum(fv) / len(fv) * 1024 * ff,
+                      "write_bytes": sum(wv) / len(wv) * 1024 * wf, "dispatches": len(fv)}
+    if "decode_v4_kernel" not in per:
+        log("no decode kernel counters found")
+        return 1
+    from head_latent_attention_05_amd import synth
+    _, alg, _ = decode_bytes_flops(synth.make_inputs(workload))
+    traffic = sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values())
+    rec = json.load(open(out)) if os.path.exists(out) else {}
+    rec[workload] = {"source_sha": source_hash(), "traffic_bytes": traffic,
+                     "algorithmic_bytes": alg, "traffic_over_algorithmic": traffic / alg,
+                     "fetch_factor": ff, "write_factor": wf, "kernels": per}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec[workload], indent=1))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,13 +314,22 @@ def main() -> int:
     ap.add_argument("--workload", default="batch64")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-workloads", default="single,long,prefill",
+                    help="comma-separated workloads whose decode call is also timed alone "
+                         "(reported under 'workloads'); empty for none")
+    ap.add_argument("--extra-calls", type=int, default=10)
     ap.add_argument("--pool-copies", type=int, default=0,
                     help="cache copies rotated between steps (0: enough for >= 1 GB)")
     ap.add_argument("--profile-decode", type=int, default=0, metavar="N",
                     help="counter-run mode: one 1 GiB device copy (the reference kernel for "
                          "scaling HBM byte counters), then N decode calls over the rotated "
                          "cache copies, nothing else; prints no JSON line")
+    ap.add_argument("--counters-json", nargs="+", metavar="DIR",
+                    help="no GPU: fold rocprofv3 --pmc output directories of the "
+                         "--profile-decode mode into profiles/decode_counters.json")
     args = ap.parse_args()
+    if args.counters_json:
+        return counters_json(args.workload, args.counters_json, COUNTERS)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (decode batches "
@@ -235,7 +415,10 @@ def main() -> int:
                  "algorithmic_bytes": int(call_bytes[k]),
                  "gbs": call_bytes[k] / (float(np.mean(v)) * 1e-3) / 1e9}
              for k, v in call_ms.items()}
-    dec_flops = reads * 2 * d.num_heads * (d.row + d.d_latent)
+    _, dec_bytes2, dec_flops = decode_bytes_flops(inp)
+    assert dec_bytes2 == dec_bytes
+    copy_gbs = copy_bandwidth(st.dev)
+    log(f"[bench] 1 GiB device copy: {copy_gbs:.0f} GB/s")
     achieved_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
     achieved_tfs = dec_flops / (dec_avg * 1e-3) / 1e12
     rec = {
@@ -261,14 +444,27 @@ def main() -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": traffic_from_counters(args.workload),
                      "algorithmic_bytes": dec_bytes, "avg_launch_us": dec_avg * 1e3,
+                     "vs_copy": {"copy_gbs": copy_gbs, "frac": achieved_gbs / copy_gbs,
+                                 "copy": "1 GiB device-to-device torch copy, same run"},
                      "mfma": {"achieved": achieved_tfs, "peak": MFMA_BF16_PEAK_TFS,
                               "unit": "TFLOP/s", "frac": achieved_tfs / MFMA_BF16_PEAK_TFS,
                               "algorithmic_flops": dec_flops}},
         "calls": calls,
     }
+    extras = [w for w in args.extra_workloads.split(",") if w and w != args.workload]
+    if extras:
+        del st, pools
+        torch.cuda.empty_cache()
+        rec["workloads"] = {}
+        for w in extras:
+            log(f"[bench] decode call alone on '{w}' ...")
+            rec["workloads"][w] = decode_only(w, args.extra_calls, 2, copy_gbs)
+            log(f"[bench]   {w}: {rec['workloads'][w]['decode_us']:.1f} us, "
+                f"{rec['workloads'][w]['hbm_frac']*100:.1f} % HBM, "
+                f"{rec['workloads'][w]['mfma_frac']*100:.1f} % MFMA")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
-        rec["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     print(json.dumps(rec), flush=True)
     return 0
 

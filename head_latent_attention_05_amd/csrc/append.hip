@@ -81,6 +81,82 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
 }
 
+// DeepSeek-V3 shapes (d_c 512, d_r 64, 128 heads), bf16: three workgroups per
+// new token.  Part 0 copies c_kv into the cache row (64 threads x 16 bytes) and
+// rotates k_pe into it (4 threads); parts 1 and 2, launched only when queries
+// are given, rotate the RoPE columns of q_lat for heads 64*(part-1) .. +63 (4
+// threads per head, each 8 rotate-half pairs i, i+32 with 16-byte loads and
+// stores).  Same fp32 op order and rounding as append_kernel, so the bytes
+// written are identical.  Every pointer must be 16-byte aligned.
+constexpr int kV3Dc = 512, kV3Dr = 64, kV3H = 128, kV3Row = 576, kV3Half = 32;
+
+__device__ __forceinline__ void rope8_bf16(const uint16_t* x, const float* cr, const float* sr,
+                                           int i0, uint16_t* y) {
+  const u32x4 a = *(const u32x4*)(x + i0);            // x[i0 .. i0+7]
+  const u32x4 b = *(const u32x4*)(x + kV3Half + i0);  // x[i0+32 .. i0+39]
+  const f32x4 c0 = *(const f32x4*)(cr + i0), c1 = *(const f32x4*)(cr + i0 + 4);
+  const f32x4 s0 = *(const f32x4*)(sr + i0), s1 = *(const f32x4*)(sr + i0 + 4);
+  uint32_t o1[4], o2[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float y1[2], y2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = 2 * k + e;  // pair i0 + j
+      const float x1 = bf16_bits_to_f32((uint16_t)(a[k] >> (16 * e)));
+      const float x2 = bf16_bits_to_f32((uint16_t)(b[k] >> (16 * e)));
+      const float c = j < 4 ? c0[j] : c1[j - 4];
+      const float sn = j < 4 ? s0[j] : s1[j - 4];
+      rope_pair(x1, x2, c, sn, y1[e], y2[e]);
+    }
+    o1[k] = (uint32_t)f32_to_bf16_bits(y1[0]) | ((uint32_t)f32_to_bf16_bits(y1[1]) << 16);
+    o2[k] = (uint32_t)f32_to_bf16_bits(y2[0]) | ((uint32_t)f32_to_bf16_bits(y2[1]) << 16);
+  }
+  *(u32x4*)(y + i0) = u32x4{o1[0], o1[1], o1[2], o1[3]};
+  *(u32x4*)(y + kV3Half + i0) = u32x4{o2[0], o2[1], o2[2], o2[3]};
+}
+
+__global__ __launch_bounds__(256) void append_v3_kernel(
+    const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
+    const uint16_t* __restrict__ q_pe, const int32_t* __restrict__ seq,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ bt, int num_seqs, int max_blocks,
+    int64_t num_blocks, const float* __restrict__ cosT, const float* __restrict__ sinT,
+    int max_pos, uint16_t* __restrict__ pool, uint16_t* __restrict__ q_lat, uint32_t* err) {
+  const int t = blockIdx.y, part = blockIdx.x, tid = threadIdx.x;
+  const int s = seq[t];
+  const int p = pos[t];
+  uint32_t bad = 0;
+  if (s < 0 || s >= num_seqs) bad |= MLA_DEVERR_SEQ;
+  if (p < 0 || p >= max_pos) bad |= MLA_DEVERR_POSITION;
+  int64_t blk = -1;
+  if (!bad) {
+    if (p / 64 >= max_blocks) {
+      bad |= MLA_DEVERR_POSITION;
+    } else {
+      blk = bt[(int64_t)s * max_blocks + p / 64];
+      if (blk < 0 || blk >= num_blocks) bad |= MLA_DEVERR_BLOCK;
+    }
+  }
+  if (bad) {
+    if (part == 0 && tid == 0 && err) atomicOr(err, bad);
+    return;
+  }
+  const float* cr = cosT + (int64_t)p * kV3Half;
+  const float* sr = sinT + (int64_t)p * kV3Half;
+  if (part > 0) {
+    const int h = 64 * (part - 1) + (tid >> 2), i0 = (tid & 3) * 8;
+    rope8_bf16(q_pe + ((int64_t)t * kV3H + h) * kV3Dr, cr, sr, i0,
+               q_lat + ((int64_t)t * kV3H + h) * kV3Row + kV3Dc);
+    return;
+  }
+  uint16_t* row = pool + (blk * 64 + p % 64) * (int64_t)kV3Row;
+  if (tid < 64) {
+    *(u32x4*)(row + 8 * tid) = *(const u32x4*)(c_kv + (int64_t)t * kV3Dc + 8 * tid);
+  } else if (tid < 68) {
+    rope8_bf16(k_pe + (int64_t)t * kV3Dr, cr, sr, (tid - 64) * 8, row + kV3Dc);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(const mla_config& c, int T, const void* c_kv, const void* k_pe,
@@ -88,6 +164,17 @@ hipError_t launch_append(const mla_config& c, int T, const void* c_kv, const voi
                          const int32_t* bt, int num_seqs, int max_blocks, int64_t num_blocks,
                          const float* cosT, const float* sinT, int max_pos, void* pool,
                          void* q_lat, uint32_t* err, hipStream_t st) {
+  const auto a16 = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+  if (c.dtype == MLA_BF16 && c.d_latent == kV3Dc && c.d_rope == kV3Dr && c.num_heads == kV3H &&
+      c.block_size == 64 && a16(c_kv) && a16(k_pe) && a16(q_pe) && a16(q_lat) && a16(pool) &&
+      a16(cosT) && a16(sinT)) {
+    // parts 1 and 2 (q_lat RoPE columns) only when queries are given
+    hipLaunchKernelGGL(append_v3_kernel, dim3(q_pe ? 3 : 1, T), dim3(256), 0, st,
+        (const uint16_t*)c_kv, (const uint16_t*)k_pe, (const uint16_t*)q_pe, seq, pos, bt,
+        num_seqs, max_blocks, num_blocks, cosT, sinT, max_pos, (uint16_t*)pool,
+        (uint16_t*)q_lat, err);
+    return hipGetLastError();
+  }
   dim3 grid(T), block(256);
   if (c.dtype == MLA_BF16) {
     hipLaunchKernelGGL(append_kernel<uint16_t>, grid, block, 0, st,

@@ -2,6 +2,7 @@
 the same seeded inputs)."""
 from __future__ import annotations
 
+import dataclasses
 import math
 
 import numpy as np
@@ -62,3 +63,40 @@ def sub_inputs(inp, seqs):
     q_start = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
     tok = np.concatenate([np.arange(inp.q_start[b], inp.q_start[b + 1]) for b in seqs])
     return q_start, tok
+
+
+def drop_queries(inp, zero):
+    """The same step with no query tokens for the sequences in `zero` (their
+    rows all become history); the other sequences' queries are unchanged."""
+    q_lens = inp.q_lens.copy()
+    keep = np.concatenate([np.full(int(q), b not in zero) for b, q in enumerate(inp.q_lens)])
+    q_lens[list(zero)] = 0
+    q_start = np.zeros(len(q_lens) + 1, np.int32)
+    q_start[1:] = np.cumsum(q_lens)
+    return dataclasses.replace(inp, q_lens=q_lens, q_start=q_start, q_nope=inp.q_nope[keep],
+                               q_pe=inp.q_pe[keep])
+
+
+def scale_rows(inp, f):
+    """The same step with every cached row of sequence b (c_kv and k_pe) scaled
+    by f(b, position): drives the logits over a wide range."""
+    c_kv, k_pe = [], []
+    for b in range(len(inp.kv_lens)):
+        s = np.array([f(b, p) for p in range(int(inp.kv_lens[b]))], np.float64)[:, None]
+        cf = synth.bf16_bits_to_f32(inp.c_kv[b]).astype(np.float64) * s
+        kf = synth.bf16_bits_to_f32(inp.k_pe[b]).astype(np.float64) * s
+        c_kv.append(synth.f32_to_bf16_bits(cf.astype(np.float32)))
+        k_pe.append(synth.f32_to_bf16_bits(kf.astype(np.float32)))
+    return dataclasses.replace(inp, c_kv=c_kv, k_pe=k_pe)
+
+
+# Row scalings that drive the logits over a wide range.  "rising": the logit
+# spread grows along the sequence to ~60x the unit spread, so the running maximum
+# grows many times by far more than any rescale threshold and, without
+# rescaling, 2^(s - m) would overflow fp32 long before the end; "falling": the
+# maximum comes first; "sink": one dominant row in the middle.
+LOGIT_PROFILES = {
+    "rising": lambda L: (lambda b, p: 1.0 + 60.0 * p / L[b]),
+    "falling": lambda L: (lambda b, p: 61.0 - 60.0 * p / L[b]),
+    "sink": lambda L: (lambda b, p: 12.0 if p == L[b] // 2 else 1.0),
+}

@@ -20,7 +20,8 @@ from head_latent_attention_05_amd import synth
 from oracle import mla_oracle as O
 from tests.emu import build_emu
 from tests.emu.emulib import Emu, EmuStep
-from tests.gpu_util import check_out, oracle_pool, pool_bits, rows_fn, sample_heads
+from tests.gpu_util import (LOGIT_PROFILES, check_out, drop_queries, oracle_pool, pool_bits,
+                            rows_fn, sample_heads, scale_rows)
 
 
 @pytest.fixture(scope="module")
@@ -64,6 +65,25 @@ def test_emu_step(emu, name):
     ref = O.naive_mla(d, inp.w_uk, inp.w_uv, inp.q_nope, inp.q_pe, rows_fn(pool, inp),
                       inp.kv_lens, inp.q_start, inp.workload.causal, heads)
     check_out(d, st.out[:, heads], ref, f"emu {name}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "v3_batch_ragged", "v3_prefill_small"])
+def test_emu_append_bit_exact(emu, name):
+    """Cache rows and the RoPE columns of q_lat written by the append kernel
+    (the vectorised DeepSeek-V3 form and the generic one) match the oracle bit
+    for bit, sentinel rows included."""
+    inp = _inputs(**CASES[name])
+    d = inp.dims
+    st = EmuStep(emu, inp)
+    st.append()
+    assert int(st.dev_error[0]) == 0
+    np.testing.assert_array_equal(pool_bits(st.pool, d), pool_bits(oracle_pool(inp), d))
+    cos, sin = O.rope_table_f32(inp.max_pos(), d.d_rope)
+    pos = inp.token_pos()
+    qpe = O.storage_to_f64(inp.q_pe, d.dtype).astype(np.float32)
+    exp = O.rope_cache_f32(qpe, cos[pos][:, None, :], sin[pos][:, None, :])
+    exp = O.to_bf16_bits(exp) if d.dtype == "bf16" else exp
+    np.testing.assert_array_equal(pool_bits(st.q_lat[:, :, d.d_latent:], d), pool_bits(exp, d))
 
 
 @pytest.mark.parametrize("name", ["tiny_prefill", "v3_batch_ragged", "v3_prefill_small",
@@ -147,26 +167,14 @@ def test_emu_bad_entries_flagged(emu):
     assert int(st.dev_error[0]) & B.DEVERR_BLOCK
 
 
-def _drop_queries(inp, zero):
-    """The same step with no query tokens for the sequences in `zero` (their
-    rows all become history); the other sequences' queries are unchanged."""
-    q_lens = inp.q_lens.copy()
-    keep = np.concatenate([np.full(int(q), b not in zero) for b, q in enumerate(inp.q_lens)])
-    q_lens[list(zero)] = 0
-    q_start = np.zeros(len(q_lens) + 1, np.int32)
-    q_start[1:] = np.cumsum(q_lens)
-    return dataclasses.replace(inp, q_lens=q_lens, q_start=q_start, q_nope=inp.q_nope[keep],
-                               q_pe=inp.q_pe[keep])
-
-
 @pytest.mark.parametrize("workload,causal,q_len", [("batch64", False, 1), ("prefill", True, 5)])
 def test_emu_sequences_without_queries(emu, workload, causal, q_len):
     """Sequences with no query tokens in the batch (empty q_start ranges) are
     skipped by the split plan, the merge and the projections."""
     inp = _inputs(workload, causal=causal, kv_lens=[100, 64, 300, 1, 129], q_len=q_len)
-    inp = _drop_queries(inp, {1, 3})
+    inp = drop_queries(inp, {1, 3})
     d = inp.dims
-    for G in (0, 3, 100000):
+    for G in (1, 2, 7, 0, 3, 100000):
         st = EmuStep(emu, inp, num_workgroups=G)
         st.run()
         assert int(st.dev_error[0]) == 0
@@ -193,7 +201,7 @@ def _random_case(rng, it):
                   seed=5000 + it)
     zero = {b for b in range(B) if rng.random() < 0.2}
     if zero and len(zero) < B:
-        inp = _drop_queries(inp, zero)
+        inp = drop_queries(inp, zero)
     G = int(rng.choice([0, 1, 2, 3, 5, 8, 13, 64, 100000]))
     return inp, G
 
@@ -224,7 +232,7 @@ def test_emu_decode_random_shapes(emu, it):
 def test_emu_more_than_64_sequences(emu, causal, q_len):
     """Batches wider than one wave: the plan walk and the merge scan the
     sequences 64 at a time."""
-    lens = [int(x) for x in np.random.default_rng(7).integers(1, 100, size=90)]
+    lens = [int(x) for x in np.random.default_rng(7).integers(1, 100, size=150)]
     inp = _inputs("batch64", causal=causal, kv_lens=lens, q_len=q_len, seed=11)
     d = inp.dims
     st = EmuStep(emu, inp)
@@ -235,23 +243,10 @@ def test_emu_more_than_64_sequences(emu, causal, q_len):
     heads = [0, 64, 127]
     ref = O.latent_decode(d, O.storage_to_f64(q, d.dtype), rows_fn(pool, inp), inp.kv_lens,
                           inp.q_start, causal, heads)
-    for G in (0, 7, 100000):
+    for G in (1, 2, 7, 0, 100000):
         st.decode(G)
         got = O.storage_to_f64(st.o_lat, d.dtype)[:, heads]
         assert np.abs(got - ref).max() <= 2.0 ** -7 * np.abs(ref).max(), G
-
-
-def _scale_rows(inp, f):
-    """The same step with every cached row of sequence b (c_kv and k_pe) scaled
-    by f(b, position): drives the logits over a wide range."""
-    c_kv, k_pe = [], []
-    for b in range(len(inp.kv_lens)):
-        s = np.array([f(b, p) for p in range(int(inp.kv_lens[b]))], np.float64)[:, None]
-        cf = synth.bf16_bits_to_f32(inp.c_kv[b]).astype(np.float64) * s
-        kf = synth.bf16_bits_to_f32(inp.k_pe[b]).astype(np.float64) * s
-        c_kv.append(synth.f32_to_bf16_bits(cf.astype(np.float32)))
-        k_pe.append(synth.f32_to_bf16_bits(kf.astype(np.float32)))
-    return dataclasses.replace(inp, c_kv=c_kv, k_pe=k_pe)
 
 
 @pytest.mark.parametrize("profile", ["rising", "falling", "sink"])
@@ -260,24 +255,18 @@ def test_emu_decode_wide_logit_range(emu, profile):
     more than the lazy-rescale threshold, many times, and by more than the fp32
     exponent range overall), fall (the maximum is found first), or have one
     dominant row in the middle."""
-    inp = _inputs("batch64", kv_lens=[700, 333])
-    L = inp.kv_lens
-    # logit spread grows to ~60x the unit spread: without rescaling, 2^(s - m)
-    # would overflow fp32 long before the end of the rising sequence
-    f = {"rising": lambda b, p: 1.0 + 60.0 * p / L[b],
-         "falling": lambda b, p: 61.0 - 60.0 * p / L[b],
-         "sink": lambda b, p: 12.0 if p == L[b] // 2 else 1.0}[profile]
-    inp = _scale_rows(inp, f)
+    inp = _inputs("batch64", kv_lens=[700, 333, 2100])
+    inp = scale_rows(inp, LOGIT_PROFILES[profile](inp.kv_lens))
     d = inp.dims
     st = EmuStep(emu, inp)
     st.append()
     q = synth.random_latent_queries(d, inp.T, seed=9)
     st.q_lat[...] = q
     pool = oracle_pool(inp)
-    heads = [0, 17, 64, 127]
+    heads = [0, 17, 63, 64, 127]
     ref = O.latent_decode(d, O.storage_to_f64(q, d.dtype), rows_fn(pool, inp), inp.kv_lens,
                           inp.q_start, False, heads)
-    for G in (1, 0, 5):
+    for G in (1, 2, 7, 0):
         st.decode(G)
         got = O.storage_to_f64(st.o_lat, d.dtype)[:, heads]
         assert np.all(np.isfinite(got))
@@ -287,7 +276,7 @@ def test_emu_decode_wide_logit_range(emu, profile):
 def test_emu_step_without_any_query(emu):
     """A batch with no query tokens at all: every call is a no-op that leaves
     its outputs untouched (only the history rows are in the cache)."""
-    inp = _drop_queries(_inputs("batch64", kv_lens=[70, 129]), {0, 1})
+    inp = drop_queries(_inputs("batch64", kv_lens=[70, 129]), {0, 1})
     assert inp.T == 0
     st = EmuStep(emu, inp)
     st.run()

@@ -16,14 +16,20 @@ pytestmark = pytest.mark.gpu
 HEADS = [0, 63, 64, 127]
 
 
-def _sample_seqs(inp, k=3):
+def _sample_seqs(inp, k=8):
+    """The first, last, longest and shortest sequences, then seeded random ones,
+    up to k distinct."""
     B = len(inp.kv_lens)
-    cand = [0, int(np.argmax(inp.kv_lens)), B - 1]
     out = []
-    for b in cand:
+    for b in [0, B - 1, int(np.argmax(inp.kv_lens)), int(np.argmin(inp.kv_lens))]:
         if b not in out:
             out.append(b)
-    return out[:k]
+    rng = np.random.default_rng(B)
+    while len(out) < min(k, B):
+        b = int(rng.integers(0, B))
+        if b not in out:
+            out.append(b)
+    return out
 
 
 @pytest.mark.parametrize("name", ["single", "batch64", "long", "prefill"])
