@@ -26,7 +26,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
 DEVERR_POSITION, DEVERR_SEQ, DEVERR_BLOCK, DEVERR_LENGTH = 1, 2, 4, 8
 
 EXPORTS = ["mla_status_string", "mla_rope_table", "mla_absorb_q", "mla_append_cache",
-           "mla_decode_workspace_size", "mla_decode", "mla_out_proj"]
+           "mla_decode_workspace_size", "mla_decode", "mla_out_proj", "mla_decode_noalloc"]
 
 
 class MlaError(RuntimeError):
@@ -66,6 +66,8 @@ def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mla_decode.argtypes = [C, I32, P, P, P, P, P, I32, I64, P, P, I32, I32, P, SZ, P, P, P]
     lib.mla_out_proj.restype = I32
     lib.mla_out_proj.argtypes = [C, I32, P, P, P, P]
+    lib.mla_decode_noalloc.restype = I32
+    lib.mla_decode_noalloc.argtypes = [C, I32, P, P, P, P, P, I32, I64, P, P, I32, I32, P, P, P]
     return lib
 
 
@@ -158,6 +160,20 @@ def decode(cfg: MlaConfig, q_start, kv_lens, q_start_host: np.ndarray, kv_lens_h
         kl.ctypes.data, _ptr(block_table), block_table.shape[1], num_pool_blocks,
         _ptr(q_lat), _ptr(kv_pool), int(causal), num_workgroups, _ptr(workspace), ws_bytes,
         _ptr(o_lat), _ptr(dev_error), _stream(stream)))
+
+
+def decode_noalloc(cfg: MlaConfig, q_start, kv_lens, q_start_host: np.ndarray,
+                   kv_lens_host: np.ndarray, block_table, num_pool_blocks: int, q_lat, kv_pool,
+                   causal: bool, o_lat, num_workgroups: int = 0, dev_error=None,
+                   stream=None) -> None:
+    lib = load()
+    qs = np.ascontiguousarray(q_start_host, np.int32)
+    kl = np.ascontiguousarray(kv_lens_host, np.int32)
+    _check("mla_decode_noalloc", lib.mla_decode_noalloc(
+        ctypes.byref(cfg), len(kl), _ptr(q_start), _ptr(kv_lens), qs.ctypes.data,
+        kl.ctypes.data, _ptr(block_table), block_table.shape[1], num_pool_blocks,
+        _ptr(q_lat), _ptr(kv_pool), int(causal), num_workgroups, _ptr(o_lat), _ptr(dev_error),
+        _stream(stream)))
 
 
 def out_proj(cfg: MlaConfig, o_lat, w_uv, out, stream=None) -> None:

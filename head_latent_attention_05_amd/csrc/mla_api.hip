@@ -114,6 +114,83 @@ mla_status plan_decode(const mla_config& c, int32_t B, const int32_t* qs, const 
   return MLA_OK;
 }
 
+// Scratch of mla_decode_noalloc: the split partials live in this array instead
+// of a caller-provided workspace.  The HIP runtime gives every device its own
+// copy when it loads the code object; host code must use the per-device address
+// from hipGetSymbolAddress, never the array's name (a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[MLA_DECODE_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per device.
+mla_status scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* cache[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> g(mu);
+  if (!cache[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MLA_ERR_HIP;
+    cache[dev] = ptr;
+  }
+  *out = cache[dev];
+  return MLA_OK;
+}
+
+// Everything of mla_decode after planning.  `workspace` holds at least
+// hp.ws_bytes bytes (checked by the caller), or is null with use_scratch set:
+// then the library's scratch is used, looked up after the argument checks.
+mla_status decode_planned(const mla_config* cfg, const HostPlan& hp, int32_t num_seqs,
+                          const int32_t* q_start, const int32_t* kv_lens,
+                          const int32_t* kv_lens_host, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, int64_t num_pool_blocks,
+                          const void* q_lat, const void* kv_pool, int32_t causal,
+                          void* workspace, bool use_scratch, void* o_lat, uint32_t* dev_error,
+                          void* stream) {
+  if (!q_start || !kv_lens || !block_table || !q_lat || !kv_pool || !o_lat)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_lat) || !aligned16(kv_pool) || !aligned16(o_lat)) return MLA_ERR_INVALID_ARG;
+  if (num_pool_blocks < 1) return MLA_ERR_INVALID_ARG;
+  int64_t maxL = 0;
+  for (int b = 0; b < num_seqs; ++b) maxL = kv_lens_host[b] > maxL ? kv_lens_host[b] : maxL;
+  if (max_blocks_per_seq < (maxL + cfg->block_size - 1) / cfg->block_size)
+    return MLA_ERR_INVALID_ARG;
+  // block-table entries are addressed with 32-bit indices on the device
+  if ((int64_t)num_seqs * max_blocks_per_seq >= ((int64_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
+  if (use_scratch && hp.ws_bytes > 0) {
+    mla_status s = scratch_ptr(&workspace);
+    if (s != MLA_OK) return s;
+  }
+  DecodeArgs a;
+  a.plan.q_start = q_start;
+  a.plan.kv_lens = kv_lens;
+  a.plan.B = num_seqs;
+  a.plan.T = hp.T;
+  a.plan.block_size = cfg->block_size;
+  a.plan.causal = causal ? 1 : 0;
+  a.plan.G = hp.G;
+  a.plan.U = hp.U;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_pool_blocks;
+  a.q_lat = q_lat;
+  a.pool = kv_pool;
+  a.o_lat = o_lat;
+  a.ws_lse = hp.ws_bytes ? (float*)workspace : nullptr;
+  a.ws_o = hp.ws_bytes ? (void*)((char*)workspace + hp.lse_bytes) : nullptr;
+  a.err = dev_error;
+  a.scale_log2 = cfg->softmax_scale * kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (is_v3_bf16(*cfg) && v3_kernels_available())
+    e = launch_decode_v3(a, st);
+  else
+    e = launch_decode_generic(*cfg, a, st);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (hp.G > 1) e = is_v3_bf16(*cfg) ? launch_merge_v3(a, st) : launch_merge(*cfg, a, st);
+  return from_hip(e);
+}
+
 }  // namespace
 }  // namespace mla
 
@@ -212,48 +289,32 @@ mla_status mla_decode(const mla_config* cfg, int32_t num_seqs, const int32_t* q_
   s = plan_decode(*cfg, num_seqs, q_start_host, kv_lens_host, causal, num_workgroups, &hp);
   if (s != MLA_OK) return s;
   if (hp.T == 0) return MLA_OK;
-  if (!q_start || !kv_lens || !block_table || !q_lat || !kv_pool || !o_lat)
-    return MLA_ERR_INVALID_ARG;
-  if (!aligned16(q_lat) || !aligned16(kv_pool) || !aligned16(o_lat)) return MLA_ERR_INVALID_ARG;
-  if (num_pool_blocks < 1) return MLA_ERR_INVALID_ARG;
-  int64_t maxL = 0;
-  for (int b = 0; b < num_seqs; ++b) maxL = kv_lens_host[b] > maxL ? kv_lens_host[b] : maxL;
-  if (max_blocks_per_seq < (maxL + cfg->block_size - 1) / cfg->block_size)
-    return MLA_ERR_INVALID_ARG;
-  // block-table entries are addressed with 32-bit indices on the device
-  if ((int64_t)num_seqs * max_blocks_per_seq >= ((int64_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
   if (hp.ws_bytes > 0) {
     if (!workspace || workspace_bytes < hp.ws_bytes || !aligned16(workspace))
       return MLA_ERR_WORKSPACE;
   }
-  DecodeArgs a;
-  a.plan.q_start = q_start;
-  a.plan.kv_lens = kv_lens;
-  a.plan.B = num_seqs;
-  a.plan.T = hp.T;
-  a.plan.block_size = cfg->block_size;
-  a.plan.causal = causal ? 1 : 0;
-  a.plan.G = hp.G;
-  a.plan.U = hp.U;
-  a.block_table = block_table;
-  a.max_blocks = max_blocks_per_seq;
-  a.num_blocks = num_pool_blocks;
-  a.q_lat = q_lat;
-  a.pool = kv_pool;
-  a.o_lat = o_lat;
-  a.ws_lse = (float*)workspace;
-  a.ws_o = workspace ? (void*)((char*)workspace + hp.lse_bytes) : nullptr;
-  a.err = dev_error;
-  a.scale_log2 = cfg->softmax_scale * kLog2e;
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
-  if (is_v3_bf16(*cfg) && v3_kernels_available())
-    e = launch_decode_v3(a, st);
-  else
-    e = launch_decode_generic(*cfg, a, st);
-  if (e != hipSuccess) return MLA_ERR_HIP;
-  if (hp.G > 1) e = is_v3_bf16(*cfg) ? launch_merge_v3(a, st) : launch_merge(*cfg, a, st);
-  return from_hip(e);
+  return decode_planned(cfg, hp, num_seqs, q_start, kv_lens, kv_lens_host, block_table,
+                        max_blocks_per_seq, num_pool_blocks, q_lat, kv_pool, causal, workspace,
+                        false, o_lat, dev_error, stream);
+}
+
+mla_status mla_decode_noalloc(const mla_config* cfg, int32_t num_seqs, const int32_t* q_start,
+                              const int32_t* kv_lens, const int32_t* q_start_host,
+                              const int32_t* kv_lens_host, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, int64_t num_pool_blocks,
+                              const void* q_lat, const void* kv_pool, int32_t causal,
+                              int32_t num_workgroups, void* o_lat, uint32_t* dev_error,
+                              void* stream) {
+  mla_status s = check_cfg(cfg);
+  if (s != MLA_OK) return s;
+  HostPlan hp;
+  s = plan_decode(*cfg, num_seqs, q_start_host, kv_lens_host, causal, num_workgroups, &hp);
+  if (s != MLA_OK) return s;
+  if (hp.T == 0) return MLA_OK;
+  if (hp.ws_bytes > MLA_DECODE_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  return decode_planned(cfg, hp, num_seqs, q_start, kv_lens, kv_lens_host, block_table,
+                        max_blocks_per_seq, num_pool_blocks, q_lat, kv_pool, causal, nullptr,
+                        true, o_lat, dev_error, stream);
 }
 
 mla_status mla_out_proj(const mla_config* cfg, int32_t T, const void* o_lat, const void* w_uv,

@@ -179,6 +179,31 @@ mla_status mla_decode(const mla_config* cfg, int32_t num_seqs, const int32_t* q_
                       int32_t num_workgroups, void* workspace, size_t workspace_bytes,
                       void* o_lat, uint32_t* dev_error, void* stream);
 
+/* Bytes of device scratch that mla_decode_noalloc owns on each device: enough
+ * for the default split plan of the DeepSeek-V3 bf16 shapes on a 256-CU MI355X
+ * (2 x 256 partial slots of [128][512] bf16 plus their fp32 log-sum-exp). */
+#define MLA_DECODE_SCRATCH_BYTES ((size_t)65 << 20)
+
+/* mla_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, math, plan, kernels and results as
+ * mla_decode (bitwise, for the same num_workgroups); the split partials go to a
+ * library-owned device array of MLA_DECODE_SCRATCH_BYTES per device (held until
+ * the process ends) instead of a workspace.  Allocates nothing: no hipMalloc,
+ * hipFree or allocating library call.  MLA_ERR_WORKSPACE when the plan needs
+ * more than MLA_DECODE_SCRATCH_BYTES (mla_decode_workspace_size tells; force a
+ * smaller num_workgroups).  Every call on one device shares that device's array:
+ * calls that overlap on one device (other streams, other host threads) race and
+ * must be serialised by the caller.  Nothing in the array needs to start at
+ * zero: each partial the merge reads is written earlier in the same call. */
+mla_status mla_decode_noalloc(const mla_config* cfg, int32_t num_seqs, const int32_t* q_start,
+                              const int32_t* kv_lens, const int32_t* q_start_host,
+                              const int32_t* kv_lens_host, const int32_t* block_table,
+                              int32_t max_blocks_per_seq, int64_t num_pool_blocks,
+                              const void* q_lat, const void* kv_pool, int32_t causal,
+                              int32_t num_workgroups, void* o_lat, uint32_t* dev_error,
+                              void* stream);
+
 /* Per-head value up-projection ([MLA explainer] forward_inference_absorbed: the
  * attended latent is mapped through W_UV per head, V is never formed):
  *   out[t][h][v] = sum_c o_lat[t][h][c] * w_uv[h][v][c]   (fp32 accumulate, fp32 out)

@@ -103,6 +103,14 @@ class Emu:
             p(block_table), block_table.shape[1], num_blocks, p(q_lat), p(pool), int(causal),
             num_workgroups, p(workspace), ws_bytes, p(o_lat), p(dev_error), None))
 
+    def decode_noalloc(self, cfg, q_start, kv_lens, block_table, num_blocks, q_lat, pool, causal,
+                       o_lat, num_workgroups=0, dev_error=None) -> None:
+        p = lambda a: None if a is None else a.ctypes.data
+        self.check("mla_decode_noalloc", self.lib.mla_decode_noalloc(
+            ctypes.byref(cfg), len(kv_lens), p(q_start), p(kv_lens), p(q_start), p(kv_lens),
+            p(block_table), block_table.shape[1], num_blocks, p(q_lat), p(pool), int(causal),
+            num_workgroups, p(o_lat), p(dev_error), None))
+
     def rope_table(self, max_pos: int, d_rope: int):
         cos = self.empty((max_pos, d_rope // 2), np.float32)
         sin = self.empty((max_pos, d_rope // 2), np.float32)

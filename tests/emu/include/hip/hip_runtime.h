@@ -11,6 +11,7 @@
 #define __shared__ static
 #define __forceinline__ inline __attribute__((always_inline))
 #define __launch_bounds__(...)
+#define __align__(n) __attribute__((aligned(n)))
 
 #define threadIdx (*::emu::g_tid)
 #define blockIdx (::emu::g_bid)
@@ -28,6 +29,13 @@ typedef enum hipDeviceAttribute_t {
 } hipDeviceAttribute_t;
 
 hipError_t hipGetLastError();
+// a file-scope __device__ array is an ordinary host array here: its address is
+// the "device" address
+#define HIP_SYMBOL(x) ((const void*)&(x))
+inline hipError_t hipGetSymbolAddress(void** p, const void* sym) {
+  *p = const_cast<void*>(sym);
+  return hipSuccess;
+}
 hipError_t hipGetDevice(int* dev);
 hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t attr, int dev);
 

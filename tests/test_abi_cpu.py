@@ -167,3 +167,27 @@ def test_decode_rejects_small_workspace_before_launch():
                         P(FAKE), 1 << 30, 100, P(FAKE), P(FAKE), 0, 8, P(FAKE), 1 << 30,
                         P(FAKE), None, None)
     assert st == 2
+
+
+def test_decode_noalloc_checks_before_launch():
+    """The allocation-free decode rejects, on the host and before any device
+    call, a plan whose partials exceed the library's scratch and the same bad
+    arguments as mla_decode."""
+    lib = B.load()
+    c = _cfg()
+    P = ctypes.c_void_p
+    qs = np.array([0, 1], np.int32)
+    kl = np.array([20000], np.int32)  # 313 cache blocks = 313 units
+    # 300 workgroups: 600 partial slots of [128][512] bf16 = 78.6 MB > 65 MiB
+    st = lib.mla_decode_noalloc(ctypes.byref(c), 1, P(FAKE), P(FAKE), qs.ctypes.data,
+                                kl.ctypes.data, P(FAKE), 313, 400, P(FAKE), P(FAKE), 0, 300,
+                                P(FAKE), None, None)
+    assert st == 3
+    # within the scratch, but the block table is too narrow
+    st = lib.mla_decode_noalloc(ctypes.byref(c), 1, P(FAKE), P(FAKE), qs.ctypes.data,
+                                kl.ctypes.data, P(FAKE), 312, 400, P(FAKE), P(FAKE), 0, 8,
+                                P(FAKE), None, None)
+    assert st == 1
+    assert lib.mla_decode_noalloc(None, 1, P(FAKE), P(FAKE), qs.ctypes.data, kl.ctypes.data,
+                                  P(FAKE), 313, 400, P(FAKE), P(FAKE), 0, 8, P(FAKE), None,
+                                  None) == 1

@@ -283,3 +283,29 @@ def test_emu_step_without_any_query(emu):
     pool = oracle_pool(inp)
     np.testing.assert_array_equal(pool_bits(st.pool, inp.dims), pool_bits(pool, inp.dims))
     assert int(st.dev_error[0]) == 0
+
+
+def test_emu_decode_noalloc_matches_decode(emu):
+    """mla_decode_noalloc (library-owned scratch) gives the bits of mla_decode
+    (caller workspace) for the same plan, on two calls in a row, the second on a
+    smaller batch; a plan needing more scratch than the library holds is
+    rejected before any launch."""
+    for kv_lens, G in (([700, 129, 1, 2000], 0), ([70, 300], 3)):
+        inp = _inputs("batch64", kv_lens=kv_lens)
+        d = inp.dims
+        st = EmuStep(emu, inp, num_workgroups=G)
+        st.append()
+        st.q_lat[...] = synth.random_latent_queries(d, inp.T, seed=4)
+        st.decode()
+        want = st.o_lat.copy()
+        st.o_lat[...] = 0
+        emu.decode_noalloc(st.cfg, st.q_start, st.kv_lens, st.block_table, st.num_blocks,
+                           st.q_lat, st.pool, False, st.o_lat, G, st.dev_error)
+        assert int(st.dev_error[0]) == 0
+        np.testing.assert_array_equal(st.o_lat, want)
+    inp = _inputs("batch64", kv_lens=[20000])
+    st = EmuStep(emu, inp)
+    with pytest.raises(B.MlaError) as e:
+        emu.decode_noalloc(st.cfg, st.q_start, st.kv_lens, st.block_table, st.num_blocks,
+                           st.q_lat, st.pool, False, st.o_lat, 300, st.dev_error)
+    assert e.value.status == 3  # MLA_ERR_WORKSPACE
