@@ -143,7 +143,7 @@ mla_status mla_append_cache(const mla_config* cfg, int32_t T, const void* c_kv,
 /* Workspace bytes that mla_decode needs for this batch (split-KV partial results).
  * Query tokens of sequence b are q_start[b] .. q_start[b+1]-1; the last of them is
  * the token at position kv_lens[b]-1.  num_workgroups = 0 lets the library choose
- * the split plan; a positive value forces that many KV workgroups (used to check
+ * the split plan; a positive value forces that many KV ranges (used to check
  * that results do not depend on the split).  Host arrays.  INVALID_ARG when a
  * length is < 1, a sequence has more query tokens than kv_len, or q_start is not
  * non-decreasing from 0. */
