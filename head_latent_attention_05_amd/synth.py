@@ -224,3 +224,26 @@ def random_latent_outputs(dims: Dims, T: int, seed: int) -> np.ndarray:
     up-projection call alone."""
     rng = np.random.default_rng(seed)
     return _store(rng.standard_normal((T, dims.num_heads, dims.d_latent)) * 0.05, dims.dtype)
+
+
+@dataclasses.dataclass
+class DownInputs:
+    """Hidden states and weights of the joint KV down-projection (storage form)."""
+    x: np.ndarray                 # [T, d_model]
+    w_dkv: np.ndarray             # [d_c + d_r, d_model] (linear layer weight)
+    b_dkv: Optional[np.ndarray]   # [d_c + d_r] or None
+    gamma: np.ndarray             # [d_c] RMSNorm gain
+    eps: float
+
+
+def make_down_inputs(dims: Dims, T: int, d_model: int, seed: int, bias: bool = True,
+                     eps: float = 1e-6) -> DownInputs:
+    """x ~ N(0, 1); W_DKV ~ N(0, 1/d_model), so each projected value is about
+    N(0, 1); bias ~ N(0, 0.1^2); gain ~ 1 + N(0, 0.1^2).  Draw order: x, W, b, gain."""
+    rng = np.random.default_rng(seed)
+    n = dims.d_latent + dims.d_rope
+    x = _store(rng.standard_normal((T, d_model)), dims.dtype)
+    w = _store(rng.standard_normal((n, d_model)) / np.sqrt(d_model), dims.dtype)
+    b = _store(rng.standard_normal(n) * 0.1, dims.dtype)
+    g = _store(1.0 + 0.1 * rng.standard_normal(dims.d_latent), dims.dtype)
+    return DownInputs(x, w, b if bias else None, g, eps)

@@ -31,7 +31,9 @@ other than itself: closed forms of the RoPE table and rotation, brute-force
 scalar loops, torch's scaled-dot-product attention, special cases, the
 absorption identity, and, for the cache rows written by append_cache, an exact
 fp64 rotation at each token's true position read back through the paged pool
-plus the relative-position property of the scores; none is "parity unpinned".
+plus the relative-position property of the scores; kv_down by brute-force
+scalar loops, one-hot inputs and closed forms of the normalisation, and the
+one-step bf16 rounding by constructed ties; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -286,6 +288,51 @@ def absorbed_mla(dims, w_uk, w_uv, q_nope, q_pe, rows_of_seq, kv_lens, q_start,
                             rope_queries(dims, q_pe, pos)], axis=-1)
     o_lat = latent_decode(dims, q_lat, rows_of_seq, kv_lens, q_start, causal, heads)
     return out_proj(dims, o_lat, w_uv, heads), o_lat
+
+
+# ----------------------------------------------------------------------------
+# Upstream of the cache: joint KV down-projection and latent RMSNorm
+# ([MLA architecture] 2.2: kv_a_proj_with_mqa maps the hidden state to
+# d_c + d_r = 576 values, the 512-d latent part goes through an RMSNorm,
+# kv_a_layernorm; the remaining 64 are the shared RoPE key before rotation)
+# ----------------------------------------------------------------------------
+
+def f64_to_bf16_bits(y: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bits, round to nearest, ties to even, in one step (no
+    intermediate fp32 rounding).  Finite normal inputs or zero."""
+    y = np.asarray(y, np.float64)
+    m, e = np.frexp(y)                      # y = m * 2^e, 0.5 <= |m| < 1
+    q = np.rint(m * 256.0)                  # 8 significant bits, half to even
+    v = np.ldexp(q, e - 8)                  # exactly representable in bf16
+    return to_bf16_bits(v.astype(np.float32))
+
+
+def round_storage(y: np.ndarray, dtype: str) -> np.ndarray:
+    """fp64 values rounded once to the storage dtype (bf16 bits or fp32)."""
+    return f64_to_bf16_bits(y) if dtype == "bf16" else np.asarray(y, np.float64).astype(np.float32)
+
+
+def rms_norm(c: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis in fp64: gamma * c / sqrt(mean(c^2) + eps)."""
+    c = np.asarray(c, np.float64)
+    return np.asarray(gamma, np.float64) * c / np.sqrt(np.mean(c * c, axis=-1, keepdims=True) + eps)
+
+
+def kv_down(dims, x, w_dkv, b_dkv, gamma, eps: float):
+    """The cache inputs of new tokens from their hidden states x [T, d_model]:
+    y = x W_DKV^T (+ b), W_DKV [d_c + d_r, d_model] (a linear layer's weight);
+    y is a tensor of the model, so it is rounded to the storage dtype; the
+    latent part is RMS-normalised with gain gamma [d_c] and rounded again.
+    Returns (c_kv [T, d_c], k_pe [T, d_r]) in storage form, ready for
+    append_cache (which rotates k_pe)."""
+    dt, dc = dims.dtype, dims.d_latent
+    y = storage_to_f64(x, dt) @ storage_to_f64(w_dkv, dt).T
+    if b_dkv is not None:
+        y = y + storage_to_f64(b_dkv, dt)
+    kv = round_storage(y, dt)
+    c = storage_to_f64(kv, dt)[:, :dc]
+    c_kv = round_storage(rms_norm(c, storage_to_f64(gamma, dt), eps), dt)
+    return c_kv, kv[:, dc:]
 
 
 # ----------------------------------------------------------------------------
