@@ -222,6 +222,66 @@ def decode_only(workload: str, calls: int, warmup: int, copy_gbs: float):
     return rec
 
 
+def upstream_calls(st, inp, calls: int, copy_gbs: float) -> dict:
+    """Calls beyond the four of the step, on the same step's new tokens, each
+    launch timed alone with HIP events; a 512 MiB fill between launches (not
+    timed) evicts the weights from L2 and the Infinity Cache, as the decode
+    between two steps would.
+
+    mla_kv_down_append: the joint KV down-projection of the new tokens' hidden
+    states (d_model 7168, synthetic) with the latent RMSNorm, fused with the
+    append.  Algorithmic bytes: the weight, the hidden states, the rows and the
+    RoPE columns of q_lat written, the query RoPE inputs read."""
+    import numpy as np
+    import torch
+
+    from head_latent_attention_05_amd import binding as B
+    from head_latent_attention_05_amd import synth
+    from head_latent_attention_05_amd.step import to_device
+
+    d = inp.dims
+    esz = 2 if d.dtype == "bf16" else 4
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=st.dev)
+    out = {}
+    if d.dtype == "bf16" and d.num_heads == 128 and d.d_latent == 512 and d.d_rope == 64:
+        d_model = 7168
+        di = synth.make_down_inputs(d, inp.T, d_model, seed=41)
+        up = lambda a: to_device(a, d.dtype, st.dev)
+        x, w, b, g = up(di.x), up(di.w_dkv), up(di.b_dkv), up(di.gamma)
+        ws = torch.empty(B.kv_down_workspace_size(st.cfg, inp.T, d_model), dtype=torch.uint8,
+                         device=st.dev)
+
+        def call():
+            B.kv_down_append(st.cfg, x, w, b, g, di.eps, st.q_pe, st.new_seq, st.new_pos,
+                             st.block_table, st.num_blocks, st.rope_cos, st.rope_sin, ws,
+                             st.pool, st.q_lat, dev_error=st.dev_error)
+
+        n = d.d_latent + d.d_rope
+        nbytes = (n * d_model + inp.T * d_model + n + d.d_latent + inp.T * d.row
+                  + 2 * inp.T * d.num_heads * d.d_rope) * esz
+        ms = []
+        for i in range(calls + 2):
+            flush.zero_()
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            e.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ms.append(a.elapsed_time(e))
+        assert int(st.dev_error.item()) == 0
+        avg = float(np.mean(ms))
+        gbs = nbytes / (avg * 1e-3) / 1e9
+        out["mla_kv_down_append"] = {
+            "avg_us": avg * 1e3, "p50_us": float(np.median(ms)) * 1e3, "calls": calls,
+            "d_model": d_model, "tokens": inp.T, "algorithmic_bytes": int(nbytes),
+            "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "copy_frac": gbs / copy_gbs,
+            "bound": "hbm"}
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 COPY_BYTES = 1 << 30
 
 
@@ -451,6 +511,9 @@ def main() -> int:
                               "algorithmic_flops": dec_flops}},
         "calls": calls,
     }
+    rec["upstream_calls"] = upstream_calls(st, inp, args.extra_calls, copy_gbs)
+    for k, v in rec["upstream_calls"].items():
+        log(f"[bench] {k}: {v['avg_us']:.1f} us, {v['hbm_frac']*100:.1f} % HBM")
     extras = [w for w in args.extra_workloads.split(",") if w and w != args.workload]
     if extras:
         del st, pools

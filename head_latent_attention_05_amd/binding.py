@@ -26,7 +26,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
 DEVERR_POSITION, DEVERR_SEQ, DEVERR_BLOCK, DEVERR_LENGTH = 1, 2, 4, 8
 
 EXPORTS = ["mla_status_string", "mla_rope_table", "mla_absorb_q", "mla_append_cache",
-           "mla_decode_workspace_size", "mla_decode", "mla_out_proj", "mla_decode_noalloc"]
+           "mla_decode_workspace_size", "mla_decode", "mla_out_proj", "mla_decode_noalloc",
+           "mla_kv_down_workspace_size", "mla_kv_down_append"]
 
 
 class MlaError(RuntimeError):
@@ -68,6 +69,11 @@ def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mla_out_proj.argtypes = [C, I32, P, P, P, P]
     lib.mla_decode_noalloc.restype = I32
     lib.mla_decode_noalloc.argtypes = [C, I32, P, P, P, P, P, I32, I64, P, P, I32, I32, P, P, P]
+    lib.mla_kv_down_workspace_size.restype = I32
+    lib.mla_kv_down_workspace_size.argtypes = [C, I32, I32, ctypes.POINTER(SZ)]
+    lib.mla_kv_down_append.restype = I32
+    lib.mla_kv_down_append.argtypes = [C, I32, I32, P, P, P, P, ctypes.c_float, P, P, P, P, I32,
+                                       I32, I64, P, P, I32, P, SZ, P, P, P, P]
     return lib
 
 
@@ -181,3 +187,25 @@ def out_proj(cfg: MlaConfig, o_lat, w_uv, out, stream=None) -> None:
     T = o_lat.shape[0]
     _check("mla_out_proj", lib.mla_out_proj(ctypes.byref(cfg), T, _ptr(o_lat), _ptr(w_uv),
                                             _ptr(out), _stream(stream)))
+
+
+def kv_down_workspace_size(cfg: MlaConfig, T: int, d_model: int) -> int:
+    lib = load()
+    out = ctypes.c_size_t(0)
+    _check("mla_kv_down_workspace_size",
+           lib.mla_kv_down_workspace_size(ctypes.byref(cfg), T, d_model, ctypes.byref(out)))
+    return out.value
+
+
+def kv_down_append(cfg: MlaConfig, x, w_dkv, b_dkv, rms_gamma, rms_eps: float, q_pe,
+                   token_seq, positions, block_table, num_pool_blocks: int, rope_cos, rope_sin,
+                   workspace, kv_pool, q_lat=None, dev_error=None, stream=None) -> None:
+    lib = load()
+    T, d_model = x.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_kv_down_append", lib.mla_kv_down_append(
+        ctypes.byref(cfg), T, d_model, _ptr(x), _ptr(w_dkv), _ptr(b_dkv), _ptr(rms_gamma),
+        float(rms_eps), _ptr(q_pe), _ptr(token_seq), _ptr(positions), _ptr(block_table),
+        block_table.shape[0], block_table.shape[1], num_pool_blocks, _ptr(rope_cos),
+        _ptr(rope_sin), rope_cos.shape[0], _ptr(workspace), ws_bytes, _ptr(kv_pool), _ptr(q_lat),
+        _ptr(dev_error), _stream(stream)))

@@ -330,4 +330,55 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t T, const void* o_lat, con
   return from_hip(launch_out_proj_generic(*cfg, T, o_lat, w_uv, out, st));
 }
 
+static mla_status check_kv_down(const mla_config* cfg, int32_t T, int32_t d_model) {
+  mla_status s = check_cfg(cfg);
+  if (s != MLA_OK) return s;
+  if (!is_v3_bf16(*cfg)) return MLA_ERR_UNSUPPORTED;
+  if (T < 0 || T > MLA_MAX_PROJ_TOKENS) return MLA_ERR_INVALID_ARG;
+  if (d_model < 512 || d_model > MLA_MAX_D_MODEL || d_model % 512 != 0) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+mla_status mla_kv_down_workspace_size(const mla_config* cfg, int32_t T, int32_t d_model,
+                                      size_t* bytes) {
+  mla_status s = check_kv_down(cfg, T, d_model);
+  if (s != MLA_OK) return s;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  *bytes = kv_down_workspace_bytes(T, d_model);
+  return MLA_OK;
+}
+
+mla_status mla_kv_down_append(const mla_config* cfg, int32_t T, int32_t d_model, const void* x,
+                              const void* w_dkv, const void* b_dkv, const void* rms_gamma,
+                              float rms_eps, const void* q_pe, const int32_t* token_seq,
+                              const int32_t* positions, const int32_t* block_table,
+                              int32_t num_seqs, int32_t max_blocks_per_seq,
+                              int64_t num_pool_blocks, const float* rope_cos,
+                              const float* rope_sin, int32_t max_pos, void* workspace,
+                              size_t workspace_bytes, void* kv_pool, void* q_lat,
+                              uint32_t* dev_error, void* stream) {
+  mla_status s = check_kv_down(cfg, T, d_model);
+  if (s != MLA_OK) return s;
+  if (!(rms_eps >= 0.f) || rms_eps > 3.0e38f) return MLA_ERR_INVALID_ARG;  // also NaN, inf
+  if (T == 0) return MLA_OK;
+  if (!x || !w_dkv || !rms_gamma || !token_seq || !positions || !block_table || !rope_cos ||
+      !rope_sin || !kv_pool)
+    return MLA_ERR_INVALID_ARG;
+  if ((q_pe == nullptr) != (q_lat == nullptr)) return MLA_ERR_INVALID_ARG;
+  if (num_seqs < 1 || max_blocks_per_seq < 1 || num_pool_blocks < 1 || max_pos < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_dkv) || !aligned16(rms_gamma) || !aligned16(kv_pool) ||
+      !aligned16(rope_cos) || !aligned16(rope_sin) || (b_dkv && !aligned16(b_dkv)) ||
+      (q_pe && (!aligned16(q_pe) || !aligned16(q_lat))))
+    return MLA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < kv_down_workspace_bytes(T, d_model) ||
+      !aligned16(workspace))
+    return MLA_ERR_WORKSPACE;
+  return from_hip(launch_kv_down_append(T, d_model, x, w_dkv, b_dkv, rms_gamma, rms_eps, q_pe,
+                                        token_seq, positions, block_table, num_seqs,
+                                        max_blocks_per_seq, num_pool_blocks, rope_cos, rope_sin,
+                                        max_pos, workspace, kv_pool, q_lat, dev_error,
+                                        (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -103,6 +103,14 @@ hipError_t launch_append(const mla_config& c, int T, const void* c_kv, const voi
                          const int32_t* bt, int num_seqs, int max_blocks, int64_t num_blocks,
                          const float* cos, const float* sin, int max_pos, void* pool,
                          void* q_lat, uint32_t* err, hipStream_t st);
+size_t kv_down_workspace_bytes(int T, int d_model);
+hipError_t launch_kv_down_append(int T, int d_model, const void* x, const void* w_dkv,
+                                 const void* b_dkv, const void* gamma, float eps,
+                                 const void* q_pe, const int32_t* seq, const int32_t* pos,
+                                 const int32_t* bt, int num_seqs, int max_blocks,
+                                 int64_t num_blocks, const float* cos, const float* sin,
+                                 int max_pos, void* workspace, void* pool, void* q_lat,
+                                 uint32_t* err, hipStream_t st);
 hipError_t launch_absorb_q(const mla_config& c, int T, const void* q_nope, const void* w_uk,
                            void* q_lat, hipStream_t st);
 hipError_t launch_out_proj(const mla_config& c, int T, const void* o_lat, const void* w_uv,

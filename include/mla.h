@@ -211,6 +211,50 @@ mla_status mla_decode_noalloc(const mla_config* cfg, int32_t num_seqs, const int
 mla_status mla_out_proj(const mla_config* cfg, int32_t T, const void* o_lat,
                         const void* w_uv, float* out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Upstream of the cache: the joint KV down-projection fused with the append.
+ * --------------------------------------------------------------------------- */
+
+/* Largest hidden size mla_kv_down_append accepts. */
+#define MLA_MAX_D_MODEL 65536
+
+/* Workspace bytes that mla_kv_down_append needs: fp32 partial sums over
+ * 512-deep slices of the hidden state, (d_model / 512) * T * (d_latent + d_rope)
+ * * 4.  Same argument checks as mla_kv_down_append. */
+mla_status mla_kv_down_workspace_size(const mla_config* cfg, int32_t T, int32_t d_model,
+                                      size_t* bytes);
+
+/* Joint KV down-projection and latent RMSNorm fused with the cache append
+ * ([MLA architecture] 2.2: kv_a_proj_with_mqa maps the hidden state to the
+ * 512-d latent and the 64-d shared RoPE key in one linear layer, and
+ * kv_a_layernorm RMS-normalises the latent; 4.2: RoPE fused with the cache
+ * update).  For each new token t (sequence token_seq[t], position positions[t]):
+ *   y[n]   = round( sum_k x[t][k] * w_dkv[n][k] + b_dkv[n] ),  n < d_latent + d_rope
+ *            (fp32 accumulation, one rounding to bf16; b_dkv may be NULL = 0)
+ *   c[i]   = round( rms_gamma[i] * y[i] / sqrt(mean_{j<d_latent} y[j]^2 + rms_eps) )
+ *   kv_pool row = [c | RoPE_p(y[d_latent:])]  with the RoPE of mla_append_cache
+ *   q_lat[t][h][d_latent:] = RoPE_p(q_pe[t][h])  as mla_append_cache (if q_pe != NULL)
+ * The normalisation is computed in fp32 (rounding may differ from an exact
+ * evaluation by one bf16 unit in the last place).
+ * x [T][d_model], w_dkv [d_latent + d_rope][d_model] (a linear layer's weight),
+ * b_dkv [d_latent + d_rope], rms_gamma [d_latent]: bf16, device, 16-byte aligned.
+ * Other arguments as mla_append_cache.  workspace: device, at least
+ * mla_kv_down_workspace_size() bytes (WORKSPACE otherwise), overwritten.
+ * Only the DeepSeek-V3 bf16 configuration is supported (UNSUPPORTED otherwise);
+ * d_model must be a positive multiple of 512, at most MLA_MAX_D_MODEL, and
+ * rms_eps finite and >= 0 (INVALID_ARG otherwise).  Entries with an
+ * out-of-range position, sequence id or block id are skipped and flagged in
+ * *dev_error. */
+mla_status mla_kv_down_append(const mla_config* cfg, int32_t T, int32_t d_model, const void* x,
+                              const void* w_dkv, const void* b_dkv, const void* rms_gamma,
+                              float rms_eps, const void* q_pe, const int32_t* token_seq,
+                              const int32_t* positions, const int32_t* block_table,
+                              int32_t num_seqs, int32_t max_blocks_per_seq,
+                              int64_t num_pool_blocks, const float* rope_cos,
+                              const float* rope_sin, int32_t max_pos, void* workspace,
+                              size_t workspace_bytes, void* kv_pool, void* q_lat,
+                              uint32_t* dev_error, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -111,6 +111,21 @@ class Emu:
             p(block_table), block_table.shape[1], num_blocks, p(q_lat), p(pool), int(causal),
             num_workgroups, p(o_lat), p(dev_error), None))
 
+    def kv_down_workspace_size(self, cfg, T, d_model) -> int:
+        out = ctypes.c_size_t(0)
+        self.check("mla_kv_down_workspace_size", self.lib.mla_kv_down_workspace_size(
+            ctypes.byref(cfg), T, d_model, ctypes.byref(out)))
+        return out.value
+
+    def kv_down_append(self, cfg, x, w_dkv, b_dkv, gamma, eps, q_pe, seq, pos, block_table,
+                       num_blocks, cos, sin, workspace, pool, q_lat=None, dev_error=None) -> None:
+        p = lambda a: None if a is None else a.ctypes.data
+        self.check("mla_kv_down_append", self.lib.mla_kv_down_append(
+            ctypes.byref(cfg), x.shape[0], x.shape[1], p(x), p(w_dkv), p(b_dkv), p(gamma),
+            float(eps), p(q_pe), p(seq), p(pos), p(block_table), block_table.shape[0],
+            block_table.shape[1], num_blocks, p(cos), p(sin), cos.shape[0], p(workspace),
+            0 if workspace is None else workspace.nbytes, p(pool), p(q_lat), p(dev_error), None))
+
     def rope_table(self, max_pos: int, d_rope: int):
         cos = self.empty((max_pos, d_rope // 2), np.float32)
         sin = self.empty((max_pos, d_rope // 2), np.float32)

@@ -100,3 +100,61 @@ LOGIT_PROFILES = {
     "falling": lambda L: (lambda b, p: 61.0 - 60.0 * p / L[b]),
     "sink": lambda L: (lambda b, p: 12.0 if p == L[b] // 2 else 1.0),
 }
+
+
+# ---------------------------------------------------------------- KV down-projection
+# Rows written from a token's hidden state go through an fp32 product and an
+# fp32 normalisation before their roundings to bf16, the oracle through fp64:
+# a value may land one bf16 unit away at a rounding boundary.  A latent value
+# then differs by at most two units, 2^-6 of itself; and the fp32 sum of d_model
+# products (about unit size, as the generator scales them) carries an absolute
+# error near sqrt(d_model) fp32 units, which a value close to zero cannot hide
+# in its own size: 2^-13 absolute covers it at d_model = 7168, while a lost or
+# repeated 512-deep slice moves a value by about 0.3.  A key value one unit off
+# moves both values of its rotated pair by up to a unit of the pair's larger
+# input, and a rotated value can be much smaller than its inputs (the two
+# products cancel), so key values are held to 2^-6 of the row's largest key
+# value.  Almost every value must still be identical.
+KV_DOWN_REL = 2.0 ** -6
+KV_DOWN_ABS = 2.0 ** -13
+KV_DOWN_MAX_DIFF_FRACTION = 0.01
+
+
+def oracle_kv_down_rows(dims, di, positions, cos32, sin32):
+    """The oracle's cache rows [T, d_c + d_r] (bf16 bits) for new tokens at
+    ``positions`` whose cache inputs come from the joint down-projection."""
+    c_kv, k_pe = O.kv_down(dims, di.x, di.w_dkv, di.b_dkv, di.gamma, di.eps)
+    T = len(positions)
+    positions = np.asarray(positions, np.int64)
+    bt = np.full((T, int(positions.max()) // 64 + 1), -1, np.int32)
+    bt[np.arange(T), positions // 64] = np.arange(T)
+    pool = O.new_pool(T, 64, dims.row, dims.dtype)
+    O.append_cache(pool, dims, 64, np.arange(T), positions, c_kv, k_pe, bt, cos32, sin32)
+    return pool[np.arange(T) * 64 + positions % 64]
+
+
+def check_kv_down_rows(got_bits: np.ndarray, exp_bits: np.ndarray, d_latent: int,
+                       label: str = "") -> None:
+    g = O.bf16_to_f64(got_bits)
+    e = O.bf16_to_f64(exp_bits)
+    assert np.all(np.isfinite(g)), f"{label}: non-finite row values"
+    scale = np.abs(e)
+    scale[:, d_latent:] = np.abs(e[:, d_latent:]).max(axis=1, keepdims=True)
+    diff = got_bits != exp_bits
+    frac = float(diff.mean())
+    bound = KV_DOWN_REL * scale + KV_DOWN_ABS
+    rel = np.abs(g - e) / bound
+    worst = float(rel[diff].max()) if diff.any() else 0.0
+    cols = np.nonzero(diff)[1]
+    print(f"[parity] {label} kv_down rows: {int(diff.sum())} of {diff.size} values differ "
+          f"({int((cols < d_latent).sum())} latent, {int((cols >= d_latent).sum())} key), "
+          f"worst {worst:.3g} of the bound", flush=True)
+    assert np.all(np.abs(g - e) <= bound), (label, worst)
+    assert frac <= KV_DOWN_MAX_DIFF_FRACTION, (label, frac)
+
+
+def kv_down_slots(inp):
+    """Physical rows of the step's new tokens."""
+    seqs, pos, _, _ = inp.new_tokens()
+    return np.array([O.slot_of(inp.block_table, int(s), int(p), 64) for s, p in zip(seqs, pos)],
+                    np.int64), pos

@@ -191,3 +191,35 @@ def test_decode_noalloc_checks_before_launch():
     assert lib.mla_decode_noalloc(None, 1, P(FAKE), P(FAKE), qs.ctypes.data, kl.ctypes.data,
                                   P(FAKE), 313, 400, P(FAKE), P(FAKE), 0, 8, P(FAKE), None,
                                   None) == 1
+
+
+def test_kv_down_argument_checks():
+    """mla_kv_down_workspace_size / mla_kv_down_append reject bad arguments
+    before any launch (fake device pointers are never dereferenced)."""
+    lib = B.load()
+    c = B.MlaConfig.from_dims(synth.V3, 64)
+    P = ctypes.c_void_p
+    out = ctypes.c_size_t(0)
+    assert lib.mla_kv_down_workspace_size(ctypes.byref(c), 64, 7168, ctypes.byref(out)) == 0
+    assert out.value == 14 * 64 * 576 * 4
+    for T, dm in ((-1, 7168), (64, 0), (64, 700), (64, 1 << 17)):
+        assert lib.mla_kv_down_workspace_size(ctypes.byref(c), T, dm, ctypes.byref(out)) == 1
+    tiny = B.MlaConfig.from_dims(synth.TINY, 64)
+    assert lib.mla_kv_down_workspace_size(ctypes.byref(tiny), 4, 512, ctypes.byref(out)) == 2
+
+    def call(cfg=c, T=4, dm=512, x=FAKE, gamma=FAKE, eps=1e-6, q_pe=None, q_lat=None, ws=FAKE,
+             ws_bytes=1 << 20, pool=FAKE, b=None):
+        return lib.mla_kv_down_append(
+            ctypes.byref(cfg), T, dm, P(x), P(FAKE), P(b), P(gamma), eps, P(q_pe), P(FAKE),
+            P(FAKE), P(FAKE), 3, 4, 10, P(FAKE), P(FAKE), 64, P(ws), ws_bytes, P(pool), P(q_lat),
+            None, None)
+
+    assert call(cfg=tiny) == 2                       # only the V3 bf16 configuration
+    assert call(dm=1000) == 1                        # not a multiple of 512
+    assert call(eps=-1.0) == 1 and call(eps=float("nan")) == 1 and call(eps=float("inf")) == 1
+    assert call(x=0) == 1 and call(gamma=0) == 1 and call(pool=0) == 1
+    assert call(q_pe=FAKE) == 1                      # q_pe without q_lat
+    assert call(x=FAKE + 2) == 1 and call(b=FAKE + 8) == 1   # not 16-byte aligned
+    assert call(ws_bytes=4 * 576 * 4 - 1) == 3       # one 512-deep slice needs 4*576 floats
+    assert call(ws=0) == 3
+    assert call(T=0, x=0, gamma=0, pool=0, ws=0) == 0   # nothing to do

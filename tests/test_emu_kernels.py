@@ -20,8 +20,9 @@ from head_latent_attention_05_amd import synth
 from oracle import mla_oracle as O
 from tests.emu import build_emu
 from tests.emu.emulib import Emu, EmuStep
-from tests.gpu_util import (LOGIT_PROFILES, check_out, drop_queries, oracle_pool, pool_bits,
-                            rows_fn, sample_heads, scale_rows)
+from tests.gpu_util import (LOGIT_PROFILES, check_kv_down_rows, check_out, drop_queries,
+                            kv_down_slots, oracle_kv_down_rows, oracle_pool, pool_bits, rows_fn,
+                            sample_heads, scale_rows)
 
 
 @pytest.fixture(scope="module")
@@ -309,3 +310,56 @@ def test_emu_decode_noalloc_matches_decode(emu):
         emu.decode_noalloc(st.cfg, st.q_start, st.kv_lens, st.block_table, st.num_blocks,
                            st.q_lat, st.pool, False, st.o_lat, 300, st.dev_error)
     assert e.value.status == 3  # MLA_ERR_WORKSPACE
+
+
+def _emu_kv_down(emu, st, inp, di, pos=None):
+    ck, kp, seq, p = st.new
+    if pos is not None:
+        p = emu.put(pos.astype(np.int32))
+    nbytes = emu.kv_down_workspace_size(st.cfg, inp.T, di.x.shape[1])
+    ws = emu.empty((nbytes,), np.uint8)
+    emu.kv_down_append(st.cfg, emu.put(di.x), emu.put(di.w_dkv),
+                       None if di.b_dkv is None else emu.put(di.b_dkv), emu.put(di.gamma), di.eps,
+                       st.q_pe, seq, p, st.block_table, st.num_blocks, st.cos, st.sin, ws,
+                       st.pool, st.q_lat, st.dev_error)
+
+
+@pytest.mark.parametrize("name,bias", [("v3_batch_ragged", True), ("v3_prefill_small", False)])
+def test_emu_kv_down_append(emu, name, bias):
+    """Joint KV down-projection + latent RMSNorm fused with the append: the new
+    rows agree with the oracle within two bf16 units (almost all identical);
+    history rows, sentinels and the q_lat RoPE columns bit for bit.  The
+    prefill case has 80 new tokens: two token tiles, the second ragged."""
+    inp = _inputs(**CASES[name])
+    d = inp.dims
+    st = EmuStep(emu, inp)
+    di = synth.make_down_inputs(d, inp.T, d_model=1024, seed=21, bias=bias)
+    _emu_kv_down(emu, st, inp, di)
+    assert int(st.dev_error[0]) == 0
+    slots, pos = kv_down_slots(inp)
+    cos32, sin32 = O.rope_table_f32(inp.max_pos(), d.d_rope)
+    got = st.pool.view(np.uint16)
+    check_kv_down_rows(got[slots], oracle_kv_down_rows(d, di, pos, cos32, sin32), d.d_latent,
+                       f"emu {name}")
+    keep = np.ones(len(got), bool)
+    keep[slots] = False
+    np.testing.assert_array_equal(got[keep], oracle_pool(inp, "history").view(np.uint16)[keep])
+    qpe = O.storage_to_f64(inp.q_pe, d.dtype).astype(np.float32)
+    exp = O.to_bf16_bits(O.rope_cache_f32(qpe, cos32[pos][:, None, :], sin32[pos][:, None, :]))
+    np.testing.assert_array_equal(st.q_lat[:, :, d.d_latent:].view(np.uint16), exp)
+
+
+def test_emu_kv_down_bad_entry_is_skipped_and_flagged(emu):
+    inp = _inputs(**CASES["v3_batch_ragged"])
+    d = inp.dims
+    st = EmuStep(emu, inp)
+    di = synth.make_down_inputs(d, inp.T, d_model=512, seed=22)
+    before = st.pool.copy()
+    _, pos = kv_down_slots(inp)
+    bad = pos.copy()
+    bad[2] = st.cos.shape[0]          # one past the RoPE table
+    _emu_kv_down(emu, st, inp, di, pos=bad)
+    assert int(st.dev_error[0]) & B.DEVERR_POSITION
+    slots, _ = kv_down_slots(inp)
+    np.testing.assert_array_equal(st.pool[slots[2]], before[slots[2]])
+    assert not np.array_equal(st.pool[slots[0]], before[slots[0]])
