@@ -247,3 +247,27 @@ def make_down_inputs(dims: Dims, T: int, d_model: int, seed: int, bias: bool = T
     b = _store(rng.standard_normal(n) * 0.1, dims.dtype)
     g = _store(1.0 + 0.1 * rng.standard_normal(dims.d_latent), dims.dtype)
     return DownInputs(x, w, b if bias else None, g, eps)
+
+
+@dataclasses.dataclass
+class FusedInputs:
+    """Inputs of the weight-level absorbed calls (storage form)."""
+    c_q: np.ndarray     # [T, d_cq] compressed queries
+    w_kq: np.ndarray    # [H, d_cq, d_c] query-side fused weight
+    o_lat: np.ndarray   # [T, H, d_c] attended latents
+    w_ov: np.ndarray    # [H, d_c, d_model] output-side fused weight
+
+
+def make_fused_inputs(dims: Dims, T: int, d_cq: int, d_model: int, seed: int) -> FusedInputs:
+    """Synthetic fused weights with the spread of the products they stand for:
+    W_UQ ~ N(0, 1/d_cq) and W_UK ~ N(0, 1/d_c) give W_KQ entries of variance
+    d_n / (d_cq d_c); W_UV ~ N(0, 1/d_c) and W_O ~ N(0, 1/(H d_v)) give W_OV
+    entries of variance 1 / (d_c H).  c_q ~ N(0, 1); o_lat as
+    random_latent_outputs.  Draw order: c_q, W_KQ, o_lat, W_OV."""
+    rng = np.random.default_rng(seed)
+    H, dc, dn = dims.num_heads, dims.d_latent, dims.d_nope
+    c_q = _store(rng.standard_normal((T, d_cq)), dims.dtype)
+    w_kq = _store(rng.standard_normal((H, d_cq, dc)) * np.sqrt(dn / (d_cq * dc)), dims.dtype)
+    o_lat = _store(rng.standard_normal((T, H, dc)) * 0.05, dims.dtype)
+    w_ov = _store(rng.standard_normal((H, dc, d_model)) / np.sqrt(dc * H), dims.dtype)
+    return FusedInputs(c_q, w_kq, o_lat, w_ov)

@@ -31,7 +31,9 @@ other than itself: closed forms of the RoPE table and rotation, brute-force
 scalar loops, torch's scaled-dot-product attention, special cases, the
 absorption identity, and, for the cache rows written by append_cache, an exact
 fp64 rotation at each token's true position read back through the paged pool
-plus the relative-position property of the scores; kv_down by brute-force
+plus the relative-position property of the scores; the weight-level
+absorption by brute-force loops and its associativity with the per-head
+calls; kv_down by brute-force
 scalar loops, one-hot inputs and closed forms of the normalisation, and the
 one-step bf16 rounding by constructed ties; none is "parity unpinned".
 """
@@ -288,6 +290,41 @@ def absorbed_mla(dims, w_uk, w_uv, q_nope, q_pe, rows_of_seq, kv_lens, q_start,
                             rope_queries(dims, q_pe, pos)], axis=-1)
     o_lat = latent_decode(dims, q_lat, rows_of_seq, kv_lens, q_start, causal, heads)
     return out_proj(dims, o_lat, w_uv, heads), o_lat
+
+
+# ----------------------------------------------------------------------------
+# Weight-level absorption ([MLA explainer] forward_inference_absorbed:
+# w_q_absorbed = W_UQ^T W_UK per head, so the compressed query c_q maps straight
+# into the latent space; w_o_absorbed = W_UV^T W_O per head, so the attended
+# latent maps straight to the model width with the sum over heads;
+# "MLA的常见问题" Q3; [MLA architecture] 3.1)
+# ----------------------------------------------------------------------------
+
+def fuse_q_weight(dims, w_uq, w_uk) -> np.ndarray:
+    """W_KQ[h, j, c] = sum_d W_UQ[h, d, j] * W_UK[h, d, c]  (fp64) [H, d_cq, d_c].
+    W_UQ [H, d_n, d_cq] maps c_q to the no-RoPE query: q_nope[t,h,d] =
+    sum_j W_UQ[h,d,j] c_q[t,j]."""
+    dt = dims.dtype
+    return np.einsum("hdj,hdc->hjc", storage_to_f64(w_uq, dt), storage_to_f64(w_uk, dt))
+
+
+def fuse_o_weight(dims, w_uv, w_o) -> np.ndarray:
+    """W_OV[h, c, m] = sum_v W_UV[h, v, c] * W_O[m, h, v]  (fp64) [H, d_c, d_model].
+    W_O [d_model, H, d_v] is the output projection over the concatenated heads."""
+    dt = dims.dtype
+    return np.einsum("hvc,mhv->hcm", storage_to_f64(w_uv, dt), storage_to_f64(w_o, dt))
+
+
+def absorb_q_fused(dims, c_q, w_kq) -> np.ndarray:
+    """q_lat[t, h, c] = sum_j c_q[t, j] * W_KQ[h, j, c]  (fp64) [T, H, d_c]."""
+    dt = dims.dtype
+    return np.einsum("tj,hjc->thc", storage_to_f64(c_q, dt), storage_to_f64(w_kq, dt))
+
+
+def out_proj_fused(dims, o_lat_f64, w_ov) -> np.ndarray:
+    """out[t, m] = sum_h sum_c o_lat[t, h, c] * W_OV[h, c, m]  (fp64) [T, d_model]."""
+    return np.einsum("thc,hcm->tm", np.asarray(o_lat_f64, np.float64),
+                     storage_to_f64(w_ov, dims.dtype))
 
 
 # ----------------------------------------------------------------------------

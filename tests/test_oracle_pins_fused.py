@@ -1,0 +1,115 @@
+"""Pins for the oracle's weight-level absorption ([MLA explainer]
+forward_inference_absorbed: w_q_absorbed and w_o_absorbed).  CPU only.
+
+Brute-force scalar loops on tiny shapes; associativity with the per-head calls
+(absorb_q, out_proj), which are pinned on their own; and the whole fused path
+against explicit-decompression attention followed by the output projection, so
+that a transposed weight, a sum over the wrong head axis or a dropped head
+fails one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+from head_latent_attention_05_amd import synth
+
+
+def _dims():
+    return synth.Dims(num_heads=3, d_latent=6, d_rope=4, d_nope=5, d_v=4, dtype="f32")
+
+
+def _w(rng, *shape):
+    return rng.standard_normal(shape).astype(np.float32)
+
+
+def test_fused_weights_match_scalar_loops():
+    d = _dims()
+    rng = np.random.default_rng(1)
+    H, dc, dn, dv, dcq, dm = 3, 6, 5, 4, 7, 8
+    w_uq, w_uk = _w(rng, H, dn, dcq), _w(rng, H, dn, dc)
+    w_uv, w_o = _w(rng, H, dv, dc), _w(rng, dm, H, dv)
+    kq = O.fuse_q_weight(d, w_uq, w_uk)
+    ov = O.fuse_o_weight(d, w_uv, w_o)
+    for h in range(H):
+        for j in range(dcq):
+            for c in range(dc):
+                v = sum(float(w_uq[h, k, j]) * float(w_uk[h, k, c]) for k in range(dn))
+                assert math.isclose(kq[h, j, c], v, rel_tol=1e-12, abs_tol=1e-12)
+        for c in range(dc):
+            for m in range(dm):
+                v = sum(float(w_uv[h, k, c]) * float(w_o[m, h, k]) for k in range(dv))
+                assert math.isclose(ov[h, c, m], v, rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_fused_calls_match_scalar_loops():
+    d = _dims()
+    rng = np.random.default_rng(2)
+    T, H, dc, dcq, dm = 2, 3, 6, 7, 8
+    c_q, w_kq = _w(rng, T, dcq), _w(rng, H, dcq, dc)
+    o_lat, w_ov = rng.standard_normal((T, H, dc)), _w(rng, H, dc, dm)
+    q = O.absorb_q_fused(d, c_q, w_kq)
+    out = O.out_proj_fused(d, o_lat, w_ov)
+    for t in range(T):
+        for h in range(H):
+            for c in range(dc):
+                v = sum(float(c_q[t, j]) * float(w_kq[h, j, c]) for j in range(dcq))
+                assert math.isclose(q[t, h, c], v, rel_tol=1e-12, abs_tol=1e-12)
+        for m in range(dm):
+            v = sum(float(o_lat[t, h, c]) * float(w_ov[h, c, m]) for h in range(H)
+                    for c in range(dc))
+            assert math.isclose(out[t, m], v, rel_tol=1e-12, abs_tol=1e-12)
+
+
+def test_query_fusion_is_associativity_with_absorb_q():
+    d = _dims()
+    rng = np.random.default_rng(3)
+    T, H, dn, dc, dcq = 4, 3, 5, 6, 9
+    c_q, w_uq, w_uk = _w(rng, T, dcq), _w(rng, H, dn, dcq), _w(rng, H, dn, dc)
+    q_nope = np.einsum("tj,hdj->thd", c_q.astype(np.float64), w_uq.astype(np.float64))
+    # both sides round one intermediate to the fp32 storage dtype: q_nope on the
+    # per-head path, the fused weight (a stored weight) on the other
+    ref = O.absorb_q(d, q_nope.astype(np.float32), w_uk)
+    got = O.absorb_q_fused(d, c_q, O.fuse_q_weight(d, w_uq, w_uk))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-6 * np.abs(ref).max())
+
+
+def test_output_fusion_is_associativity_with_out_proj():
+    d = _dims()
+    rng = np.random.default_rng(4)
+    T, H, dv, dc, dm = 3, 3, 4, 6, 10
+    o_lat, w_uv, w_o = rng.standard_normal((T, H, dc)), _w(rng, H, dv, dc), _w(rng, dm, H, dv)
+    per_head = O.out_proj(d, o_lat, w_uv)                      # [T, H, d_v]
+    ref = np.einsum("thv,mhv->tm", per_head, w_o.astype(np.float64))
+    got = O.out_proj_fused(d, o_lat, O.fuse_o_weight(d, w_uv, w_o))   # weight stored as fp32
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-6 * np.abs(ref).max())
+
+
+def test_fused_path_equals_explicit_decompression_then_output_projection():
+    """The explainer's self-test in spirit: forward_training (decompress K and V,
+    attend, project with W_O) against the fused-weight absorbed path."""
+    d = synth.Dims(num_heads=2, d_latent=8, d_rope=4, d_nope=6, d_v=5, dtype="f32")
+    rng = np.random.default_rng(5)
+    H, dc, dr, dn, dv, dcq, dm = 2, 8, 4, 6, 5, 10, 7
+    lens = [9, 4]
+    rows = [rng.standard_normal((L, dc + dr)) for L in lens]
+    q_start = np.array([0, 2, 3])
+    T = 3
+    c_q = _w(rng, T, dcq)
+    w_uq = (_w(rng, H, dn, dcq) / math.sqrt(dcq)).astype(np.float32)
+    w_uk = (_w(rng, H, dn, dc) / math.sqrt(dc)).astype(np.float32)
+    w_uv = (_w(rng, H, dv, dc) / math.sqrt(dc)).astype(np.float32)
+    w_o = (_w(rng, dm, H, dv) / math.sqrt(H * dv)).astype(np.float32)
+    q_pe = _w(rng, T, H, dr)
+    q_nope = np.einsum("tj,hdj->thd", c_q.astype(np.float64), w_uq.astype(np.float64))
+    rows_fn = lambda b: rows[b]
+    naive = O.naive_mla(d, w_uk, w_uv, q_nope, q_pe, rows_fn, np.array(lens), q_start, True)
+    ref = np.einsum("thv,mhv->tm", naive, w_o.astype(np.float64))
+    pos = np.array([7, 8, 3])   # kv_len - q_len + j
+    q_lat = np.concatenate([O.absorb_q_fused(d, c_q, O.fuse_q_weight(d, w_uq, w_uk)),
+                            O.rope_queries(d, q_pe, pos)], axis=-1)
+    o_lat = O.latent_decode(d, q_lat, rows_fn, np.array(lens), q_start, True)
+    got = O.out_proj_fused(d, o_lat, O.fuse_o_weight(d, w_uv, w_o))
+    # the fused weights are stored weights (rounded to fp32 here)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-6 * np.abs(ref).max())
