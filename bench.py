@@ -224,14 +224,18 @@ def decode_only(workload: str, calls: int, warmup: int, copy_gbs: float):
 
 def upstream_calls(st, inp, calls: int, copy_gbs: float) -> dict:
     """Calls beyond the four of the step, on the same step's new tokens, each
-    launch timed alone with HIP events; a 512 MiB fill between launches (not
+    launch timed alone with HIP events; a 1 GiB read between launches (not
     timed) evicts the weights from L2 and the Infinity Cache, as the decode
-    between two steps would.
+    between two steps would.  (A fill would leave dirty lines whose write-back
+    overlaps the timed call.)
 
     mla_kv_down_append: the joint KV down-projection of the new tokens' hidden
     states (d_model 7168, synthetic) with the latent RMSNorm, fused with the
     append.  Algorithmic bytes: the weight, the hidden states, the rows and the
-    RoPE columns of q_lat written, the query RoPE inputs read."""
+    RoPE columns of q_lat written, the query RoPE inputs read.
+    mla_absorb_q_fused / mla_out_proj_fused: the weight-level absorbed
+    projections with synthetic fused weights (d_cq 1536, d_model 7168); bytes:
+    the fused weight plus the activations in and out."""
     import numpy as np
     import torch
 
@@ -241,7 +245,7 @@ def upstream_calls(st, inp, calls: int, copy_gbs: float) -> dict:
 
     d = inp.dims
     esz = 2 if d.dtype == "bf16" else 4
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=st.dev)
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=st.dev)
     out = {}
     if d.dtype == "bf16" and d.num_heads == 128 and d.d_latent == 512 and d.d_rope == 64:
         d_model = 7168
@@ -261,7 +265,7 @@ def upstream_calls(st, inp, calls: int, copy_gbs: float) -> dict:
                   + 2 * inp.T * d.num_heads * d.d_rope) * esz
         ms = []
         for i in range(calls + 2):
-            flush.zero_()
+            flush.sum()
             a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             call()
@@ -277,6 +281,42 @@ def upstream_calls(st, inp, calls: int, copy_gbs: float) -> dict:
             "d_model": d_model, "tokens": inp.T, "algorithmic_bytes": int(nbytes),
             "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "copy_frac": gbs / copy_gbs,
             "bound": "hbm"}
+        # weight-level absorption: the fused query-side and output-side weights
+        d_cq = 1536
+        fi = synth.make_fused_inputs(d, inp.T, d_cq, d_model, seed=42)
+        c_q, w_kq = up(fi.c_q), up(fi.w_kq)
+        o_lat, w_ov = up(fi.o_lat), up(fi.w_ov)
+        q_lat = torch.empty_like(st.q_lat)
+        out_f = torch.empty((inp.T, d_model), dtype=torch.float32, device=st.dev)
+        ws_f = torch.empty(B.out_proj_fused_workspace_size(st.cfg, inp.T, d_model),
+                           dtype=torch.uint8, device=st.dev)
+        H, dc = d.num_heads, d.d_latent
+        fused = {
+            "mla_absorb_q_fused": (lambda: B.absorb_q_fused(st.cfg, c_q, w_kq, q_lat),
+                                   (H * d_cq * dc + inp.T * d_cq + inp.T * H * dc) * esz,
+                                   {"d_cq": d_cq}),
+            "mla_out_proj_fused": (lambda: B.out_proj_fused(st.cfg, o_lat, w_ov, out_f, ws_f),
+                                   (H * dc * d_model + inp.T * H * dc) * esz
+                                   + inp.T * d_model * 4, {"d_model": d_model}),
+        }
+        for name, (fn, nb, extra) in fused.items():
+            ms = []
+            for i in range(calls + 2):
+                flush.sum()
+                a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                e.record()
+                torch.cuda.synchronize()
+                if i >= 2:
+                    ms.append(a.elapsed_time(e))
+            avg = float(np.mean(ms))
+            gbs = nb / (avg * 1e-3) / 1e9
+            out[name] = {"avg_us": avg * 1e3, "p50_us": float(np.median(ms)) * 1e3,
+                         "calls": calls, "tokens": inp.T, "algorithmic_bytes": int(nb),
+                         "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "copy_frac": gbs / copy_gbs,
+                         "bound": "hbm", **extra}
+        del c_q, w_kq, o_lat, w_ov, q_lat, out_f, ws_f
     del flush
     torch.cuda.empty_cache()
     return out

@@ -27,7 +27,8 @@ DEVERR_POSITION, DEVERR_SEQ, DEVERR_BLOCK, DEVERR_LENGTH = 1, 2, 4, 8
 
 EXPORTS = ["mla_status_string", "mla_rope_table", "mla_absorb_q", "mla_append_cache",
            "mla_decode_workspace_size", "mla_decode", "mla_out_proj", "mla_decode_noalloc",
-           "mla_kv_down_workspace_size", "mla_kv_down_append"]
+           "mla_kv_down_workspace_size", "mla_kv_down_append", "mla_absorb_q_fused",
+           "mla_out_proj_fused_workspace_size", "mla_out_proj_fused"]
 
 
 class MlaError(RuntimeError):
@@ -69,6 +70,12 @@ def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mla_out_proj.argtypes = [C, I32, P, P, P, P]
     lib.mla_decode_noalloc.restype = I32
     lib.mla_decode_noalloc.argtypes = [C, I32, P, P, P, P, P, I32, I64, P, P, I32, I32, P, P, P]
+    lib.mla_absorb_q_fused.restype = I32
+    lib.mla_absorb_q_fused.argtypes = [C, I32, I32, P, P, P, P]
+    lib.mla_out_proj_fused_workspace_size.restype = I32
+    lib.mla_out_proj_fused_workspace_size.argtypes = [C, I32, I32, ctypes.POINTER(SZ)]
+    lib.mla_out_proj_fused.restype = I32
+    lib.mla_out_proj_fused.argtypes = [C, I32, I32, P, P, P, P, SZ, P]
     lib.mla_kv_down_workspace_size.restype = I32
     lib.mla_kv_down_workspace_size.argtypes = [C, I32, I32, ctypes.POINTER(SZ)]
     lib.mla_kv_down_append.restype = I32
@@ -209,3 +216,28 @@ def kv_down_append(cfg: MlaConfig, x, w_dkv, b_dkv, rms_gamma, rms_eps: float, q
         block_table.shape[0], block_table.shape[1], num_pool_blocks, _ptr(rope_cos),
         _ptr(rope_sin), rope_cos.shape[0], _ptr(workspace), ws_bytes, _ptr(kv_pool), _ptr(q_lat),
         _ptr(dev_error), _stream(stream)))
+
+
+def absorb_q_fused(cfg: MlaConfig, c_q, w_kq, q_lat, stream=None) -> None:
+    lib = load()
+    T, d_cq = c_q.shape
+    _check("mla_absorb_q_fused", lib.mla_absorb_q_fused(
+        ctypes.byref(cfg), T, d_cq, _ptr(c_q), _ptr(w_kq), _ptr(q_lat), _stream(stream)))
+
+
+def out_proj_fused_workspace_size(cfg: MlaConfig, T: int, d_model: int) -> int:
+    lib = load()
+    out = ctypes.c_size_t(0)
+    _check("mla_out_proj_fused_workspace_size", lib.mla_out_proj_fused_workspace_size(
+        ctypes.byref(cfg), T, d_model, ctypes.byref(out)))
+    return out.value
+
+
+def out_proj_fused(cfg: MlaConfig, o_lat, w_ov, out, workspace, stream=None) -> None:
+    lib = load()
+    T = o_lat.shape[0]
+    d_model = out.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_out_proj_fused", lib.mla_out_proj_fused(
+        ctypes.byref(cfg), T, d_model, _ptr(o_lat), _ptr(w_ov), _ptr(out), _ptr(workspace),
+        ws_bytes, _stream(stream)))

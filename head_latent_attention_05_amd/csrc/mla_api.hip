@@ -330,6 +330,49 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t T, const void* o_lat, con
   return from_hip(launch_out_proj_generic(*cfg, T, o_lat, w_uv, out, st));
 }
 
+static mla_status check_fused(const mla_config* cfg, int32_t T, int32_t width, int32_t mult) {
+  mla_status s = check_cfg(cfg);
+  if (s != MLA_OK) return s;
+  if (!is_v3_bf16(*cfg)) return MLA_ERR_UNSUPPORTED;
+  if (T < 0 || T > MLA_MAX_PROJ_TOKENS) return MLA_ERR_INVALID_ARG;
+  if (width < mult || width > MLA_MAX_D_MODEL || width % mult != 0) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+mla_status mla_absorb_q_fused(const mla_config* cfg, int32_t T, int32_t d_cq, const void* c_q,
+                              const void* w_kq, void* q_lat, void* stream) {
+  mla_status s = check_fused(cfg, T, d_cq, 128);
+  if (s != MLA_OK) return s;
+  if (T == 0) return MLA_OK;
+  if (!c_q || !w_kq || !q_lat) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(c_q) || !aligned16(w_kq) || !aligned16(q_lat)) return MLA_ERR_INVALID_ARG;
+  return from_hip(launch_absorb_q_fused(T, d_cq, c_q, w_kq, q_lat, (hipStream_t)stream));
+}
+
+mla_status mla_out_proj_fused_workspace_size(const mla_config* cfg, int32_t T,
+                                             int32_t d_model, size_t* bytes) {
+  mla_status s = check_fused(cfg, T, d_model, 256);
+  if (s != MLA_OK) return s;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  *bytes = out_fused_workspace_bytes(T, d_model);
+  return MLA_OK;
+}
+
+mla_status mla_out_proj_fused(const mla_config* cfg, int32_t T, int32_t d_model,
+                              const void* o_lat, const void* w_ov, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  mla_status s = check_fused(cfg, T, d_model, 256);
+  if (s != MLA_OK) return s;
+  if (T == 0) return MLA_OK;
+  if (!o_lat || !w_ov || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(o_lat) || !aligned16(w_ov) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < out_fused_workspace_bytes(T, d_model) ||
+      !aligned16(workspace))
+    return MLA_ERR_WORKSPACE;
+  return from_hip(
+      launch_out_proj_fused(T, d_model, o_lat, w_ov, out, workspace, (hipStream_t)stream));
+}
+
 static mla_status check_kv_down(const mla_config* cfg, int32_t T, int32_t d_model) {
   mla_status s = check_cfg(cfg);
   if (s != MLA_OK) return s;

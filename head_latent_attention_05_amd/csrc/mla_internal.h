@@ -103,6 +103,11 @@ hipError_t launch_append(const mla_config& c, int T, const void* c_kv, const voi
                          const int32_t* bt, int num_seqs, int max_blocks, int64_t num_blocks,
                          const float* cos, const float* sin, int max_pos, void* pool,
                          void* q_lat, uint32_t* err, hipStream_t st);
+size_t out_fused_workspace_bytes(int T, int d_model);
+hipError_t launch_absorb_q_fused(int T, int d_cq, const void* c_q, const void* w_kq, void* q_lat,
+                                 hipStream_t st);
+hipError_t launch_out_proj_fused(int T, int d_model, const void* o_lat, const void* w_ov,
+                                 float* out, void* workspace, hipStream_t st);
 size_t kv_down_workspace_bytes(int T, int d_model);
 hipError_t launch_kv_down_append(int T, int d_model, const void* x, const void* w_dkv,
                                  const void* b_dkv, const void* gamma, float eps,

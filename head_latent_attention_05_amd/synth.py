@@ -258,6 +258,22 @@ class FusedInputs:
     w_ov: np.ndarray    # [H, d_c, d_model] output-side fused weight
 
 
+def _normal_store(rng, shape, std: float, dtype: str) -> np.ndarray:
+    """N(0, std^2) values in storage form, drawn in fp32 and converted in
+    chunks (the fused weights run to hundreds of MB)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint16 if dtype == "bf16" else np.float32)
+    step = 1 << 24
+    for a in range(0, n, step):
+        x = rng.standard_normal(min(step, n - a), dtype=np.float32) * np.float32(std)
+        if dtype == "bf16":
+            u = x.view(np.uint32)   # finite, so u + 0x8000 does not wrap
+            x = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+                 >> np.uint32(16)).astype(np.uint16)
+        out[a:a + len(x)] = x
+    return out.reshape(shape)
+
+
 def make_fused_inputs(dims: Dims, T: int, d_cq: int, d_model: int, seed: int) -> FusedInputs:
     """Synthetic fused weights with the spread of the products they stand for:
     W_UQ ~ N(0, 1/d_cq) and W_UK ~ N(0, 1/d_c) give W_KQ entries of variance
@@ -265,9 +281,9 @@ def make_fused_inputs(dims: Dims, T: int, d_cq: int, d_model: int, seed: int) ->
     entries of variance 1 / (d_c H).  c_q ~ N(0, 1); o_lat as
     random_latent_outputs.  Draw order: c_q, W_KQ, o_lat, W_OV."""
     rng = np.random.default_rng(seed)
-    H, dc, dn = dims.num_heads, dims.d_latent, dims.d_nope
-    c_q = _store(rng.standard_normal((T, d_cq)), dims.dtype)
-    w_kq = _store(rng.standard_normal((H, d_cq, dc)) * np.sqrt(dn / (d_cq * dc)), dims.dtype)
-    o_lat = _store(rng.standard_normal((T, H, dc)) * 0.05, dims.dtype)
-    w_ov = _store(rng.standard_normal((H, dc, d_model)) / np.sqrt(dc * H), dims.dtype)
+    H, dc, dn, dt = dims.num_heads, dims.d_latent, dims.d_nope, dims.dtype
+    c_q = _normal_store(rng, (T, d_cq), 1.0, dt)
+    w_kq = _normal_store(rng, (H, d_cq, dc), float(np.sqrt(dn / (d_cq * dc))), dt)
+    o_lat = _normal_store(rng, (T, H, dc), 0.05, dt)
+    w_ov = _normal_store(rng, (H, dc, d_model), float(1.0 / np.sqrt(dc * H)), dt)
     return FusedInputs(c_q, w_kq, o_lat, w_ov)

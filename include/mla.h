@@ -212,11 +212,50 @@ mla_status mla_out_proj(const mla_config* cfg, int32_t T, const void* o_lat,
                         const void* w_uv, float* out, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Upstream of the cache: the joint KV down-projection fused with the append.
+ * Weight-level absorption: the query-side and output-side fused weights.
  * --------------------------------------------------------------------------- */
 
-/* Largest hidden size mla_kv_down_append accepts. */
+/* Largest model width (and compressed-query width) the fused-weight calls and
+ * mla_kv_down_append accept. */
 #define MLA_MAX_D_MODEL 65536
+
+/* Query absorption with the fused weight ([MLA explainer]
+ * forward_inference_absorbed, w_q_absorbed = W_UQ^T W_UK per head: the
+ * compressed query c_q goes straight into the latent space):
+ *   q_lat[t][h][c] = round( sum_j c_q[t][j] * w_kq[h][j][c] ),  c < d_latent
+ * c_q [T][d_cq], w_kq [H][d_cq][d_latent] (W_KQ[h][j][c] = sum_d W_UQ[h][d][j] *
+ * W_UK[h][d][c], prepared by the caller), q_lat as mla_absorb_q (columns
+ * [0, d_latent) written).  fp32 accumulation, one rounding (nearest even).
+ * Only the DeepSeek-V3 bf16 configuration (UNSUPPORTED otherwise); d_cq a
+ * positive multiple of 128, at most MLA_MAX_D_MODEL; T as mla_absorb_q
+ * (INVALID_ARG otherwise).  Device pointers, 16-byte aligned. */
+mla_status mla_absorb_q_fused(const mla_config* cfg, int32_t T, int32_t d_cq, const void* c_q,
+                              const void* w_kq, void* q_lat, void* stream);
+
+/* Workspace bytes for mla_out_proj_fused: fp32 partial sums of 16 ranges of
+ * the contraction, 16 * T * d_model * 4.  Same argument checks as the call. */
+mla_status mla_out_proj_fused_workspace_size(const mla_config* cfg, int32_t T,
+                                             int32_t d_model, size_t* bytes);
+
+/* Output projection with the fused weight ([MLA explainer]
+ * forward_inference_absorbed, w_o_absorbed = W_UV^T W_O per head: the attended
+ * latent goes straight to the model width, summed over the heads):
+ *   out[t][m] = sum_h sum_c o_lat[t][h][c] * w_ov[h][c][m]     (fp32 out)
+ * o_lat [T][H][d_latent], w_ov [H][d_latent][d_model] (W_OV[h][c][m] =
+ * sum_v W_UV[h][v][c] * W_O[m][h][v], prepared by the caller), out [T][d_model].
+ * The contraction over (h, c) is split into 16 ranges whose fp32 partial sums
+ * go to the workspace and are added in a fixed order (results are run-to-run
+ * bitwise deterministic).  workspace: device, at least
+ * mla_out_proj_fused_workspace_size() bytes (WORKSPACE otherwise).  Only the
+ * DeepSeek-V3 bf16 configuration; d_model a positive multiple of 256, at most
+ * MLA_MAX_D_MODEL; T as mla_out_proj.  Device pointers, 16-byte aligned. */
+mla_status mla_out_proj_fused(const mla_config* cfg, int32_t T, int32_t d_model,
+                              const void* o_lat, const void* w_ov, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Upstream of the cache: the joint KV down-projection fused with the append.
+ * --------------------------------------------------------------------------- */
 
 /* Workspace bytes that mla_kv_down_append needs: fp32 partial sums over
  * 512-deep slices of the hidden state, (d_model / 512) * T * (d_latent + d_rope)

@@ -321,10 +321,14 @@ def absorb_q_fused(dims, c_q, w_kq) -> np.ndarray:
     return np.einsum("tj,hjc->thc", storage_to_f64(c_q, dt), storage_to_f64(w_kq, dt))
 
 
-def out_proj_fused(dims, o_lat_f64, w_ov) -> np.ndarray:
-    """out[t, m] = sum_h sum_c o_lat[t, h, c] * W_OV[h, c, m]  (fp64) [T, d_model]."""
+def out_proj_fused(dims, o_lat_f64, w_ov, cols: Optional[list] = None) -> np.ndarray:
+    """out[t, m] = sum_h sum_c o_lat[t, h, c] * W_OV[h, c, m]  (fp64) [T, d_model],
+    or only the columns m in ``cols``."""
+    w = np.asarray(w_ov)
+    if cols is not None:
+        w = w[:, :, list(cols)]
     return np.einsum("thc,hcm->tm", np.asarray(o_lat_f64, np.float64),
-                     storage_to_f64(w_ov, dims.dtype))
+                     storage_to_f64(w, dims.dtype))
 
 
 # ----------------------------------------------------------------------------

@@ -111,6 +111,21 @@ class Emu:
             p(block_table), block_table.shape[1], num_blocks, p(q_lat), p(pool), int(causal),
             num_workgroups, p(o_lat), p(dev_error), None))
 
+    def absorb_q_fused(self, cfg, c_q, w_kq, q_lat) -> None:
+        self.check("mla_absorb_q_fused", self.lib.mla_absorb_q_fused(
+            ctypes.byref(cfg), c_q.shape[0], c_q.shape[1], c_q.ctypes.data, w_kq.ctypes.data,
+            q_lat.ctypes.data, None))
+
+    def out_proj_fused(self, cfg, o_lat, w_ov, out) -> None:
+        T, d_model = out.shape
+        n = ctypes.c_size_t(0)
+        self.check("mla_out_proj_fused_workspace_size", self.lib.mla_out_proj_fused_workspace_size(
+            ctypes.byref(cfg), T, d_model, ctypes.byref(n)))
+        ws = self.empty((n.value,), np.uint8)
+        self.check("mla_out_proj_fused", self.lib.mla_out_proj_fused(
+            ctypes.byref(cfg), T, d_model, o_lat.ctypes.data, w_ov.ctypes.data, out.ctypes.data,
+            ws.ctypes.data, ws.nbytes, None))
+
     def kv_down_workspace_size(self, cfg, T, d_model) -> int:
         out = ctypes.c_size_t(0)
         self.check("mla_kv_down_workspace_size", self.lib.mla_kv_down_workspace_size(

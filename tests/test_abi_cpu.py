@@ -223,3 +223,28 @@ def test_kv_down_argument_checks():
     assert call(ws_bytes=4 * 576 * 4 - 1) == 3       # one 512-deep slice needs 4*576 floats
     assert call(ws=0) == 3
     assert call(T=0, x=0, gamma=0, pool=0, ws=0) == 0   # nothing to do
+
+
+def test_fused_weight_argument_checks():
+    lib = B.load()
+    c = B.MlaConfig.from_dims(synth.V3, 64)
+    tiny = B.MlaConfig.from_dims(synth.TINY, 64)
+    P = ctypes.c_void_p
+    F = P(FAKE)
+    assert lib.mla_absorb_q_fused(ctypes.byref(tiny), 4, 1536, F, F, F, None) == 2
+    assert lib.mla_absorb_q_fused(ctypes.byref(c), 4, 1000, F, F, F, None) == 1
+    assert lib.mla_absorb_q_fused(ctypes.byref(c), -1, 1536, F, F, F, None) == 1
+    assert lib.mla_absorb_q_fused(ctypes.byref(c), 4, 1536, None, F, F, None) == 1
+    assert lib.mla_absorb_q_fused(ctypes.byref(c), 4, 1536, P(FAKE + 2), F, F, None) == 1
+    assert lib.mla_absorb_q_fused(ctypes.byref(c), 0, 1536, None, None, None, None) == 0
+    out = ctypes.c_size_t(0)
+    assert lib.mla_out_proj_fused_workspace_size(ctypes.byref(c), 64, 7168,
+                                                 ctypes.byref(out)) == 0
+    assert out.value == 16 * 64 * 7168 * 4
+    assert lib.mla_out_proj_fused_workspace_size(ctypes.byref(c), 64, 7000,
+                                                 ctypes.byref(out)) == 1
+    assert lib.mla_out_proj_fused(ctypes.byref(c), 4, 7168, F, F, F, F, 16 * 4 * 7168 * 4 - 1,
+                                  None) == 3
+    assert lib.mla_out_proj_fused(ctypes.byref(c), 4, 7168, F, F, F, None, 1 << 30, None) == 3
+    assert lib.mla_out_proj_fused(ctypes.byref(c), 4, 7168, F, None, F, F, 1 << 30, None) == 1
+    assert lib.mla_out_proj_fused(ctypes.byref(tiny), 4, 7168, F, F, F, F, 1 << 30, None) == 2

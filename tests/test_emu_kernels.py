@@ -363,3 +363,23 @@ def test_emu_kv_down_bad_entry_is_skipped_and_flagged(emu):
     slots, _ = kv_down_slots(inp)
     np.testing.assert_array_equal(st.pool[slots[2]], before[slots[2]])
     assert not np.array_equal(st.pool[slots[0]], before[slots[0]])
+
+
+@pytest.mark.parametrize("T", [5, 70])
+def test_emu_fused_weight_projections(emu, T):
+    """Weight-level absorbed calls (fused W_KQ and W_OV streamed through LDS)
+    over one and two token tiles, against the oracle's definitions."""
+    d = synth.V3
+    cfg = B.MlaConfig.from_dims(d)
+    fi = synth.make_fused_inputs(d, T, d_cq=256, d_model=512, seed=9)
+    q_lat = emu.empty((T, d.num_heads, d.row), np.uint16)
+    q_lat[...] = 0x7FC1   # RoPE columns must stay untouched
+    emu.absorb_q_fused(cfg, emu.put(fi.c_q), emu.put(fi.w_kq), q_lat)
+    ref = O.absorb_q_fused(d, fi.c_q, fi.w_kq)
+    got = O.storage_to_f64(q_lat[:, :, :d.d_latent], d.dtype)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-5 * np.abs(ref).max())
+    assert np.all(q_lat[:, :, d.d_latent:] == 0x7FC1)
+    out = emu.empty((T, 512), np.float32)
+    emu.out_proj_fused(cfg, emu.put(fi.o_lat), emu.put(fi.w_ov), out)
+    ref = O.out_proj_fused(d, O.storage_to_f64(fi.o_lat, d.dtype), fi.w_ov)
+    assert np.abs(out - ref).max() <= 5e-5 * np.abs(ref).max()

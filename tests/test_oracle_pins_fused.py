@@ -60,6 +60,8 @@ def test_fused_calls_match_scalar_loops():
             v = sum(float(o_lat[t, h, c]) * float(w_ov[h, c, m]) for h in range(H)
                     for c in range(dc))
             assert math.isclose(out[t, m], v, rel_tol=1e-12, abs_tol=1e-12)
+    cols = [6, 1, 3]
+    np.testing.assert_allclose(O.out_proj_fused(d, o_lat, w_ov, cols), out[:, cols], rtol=1e-13)
 
 
 def test_query_fusion_is_associativity_with_absorb_q():
