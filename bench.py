@@ -217,6 +217,8 @@ def decode_only(workload: str, calls: int, warmup: int, copy_gbs: float):
            "mfma_tfs": tfs, "mfma_frac": tfs / MFMA_BF16_PEAK_TFS,
            "bound": "mfma" if inp.workload.causal and inp.T > len(inp.kv_lens) else "hbm",
            "cache_copies_rotated": len(pools)}
+    if inp.workload.causal and inp.T > len(inp.kv_lens) and inp.dims.dtype == "bf16":
+        rec["decompressed"] = decompressed_only(st, inp, pools, calls, reads)
     del st, pools
     torch.cuda.empty_cache()
     return rec
@@ -320,6 +322,50 @@ def upstream_calls(st, inp, calls: int, copy_gbs: float) -> dict:
     del flush
     torch.cuda.empty_cache()
     return out
+
+
+def decompressed_only(st, inp, pools, calls: int, pairs: int) -> dict:
+    """The same prefill through mla_prefill_decompressed (explicit decompression
+    of K and V, then attention at widths 192 / 128).  Algorithmic FLOPs: the
+    decompression of every cached row of the batch for every head
+    (2 * rows * d_c * (d_nope + d_v) * H) plus 2 * H * (d_nope + d_rope + d_v)
+    per attended (query, key) pair."""
+    import numpy as np
+    import torch
+
+    from head_latent_attention_05_amd import binding as B
+
+    d = inp.dims
+    ws = torch.empty(B.prefill_workspace_size(st.cfg, st.q_start_host, st.kv_lens_host),
+                     dtype=torch.uint8, device=st.dev)
+    out = torch.empty((inp.T, d.num_heads, d.d_v), dtype=torch.float32, device=st.dev)
+
+    def call(pool):
+        B.prefill_decompressed(st.cfg, st.q_start, st.kv_lens, st.q_start_host, st.kv_lens_host,
+                               st.block_table, st.num_blocks, st.q_nope, st.q_lat, pool, st.w_uk,
+                               st.w_uv, st.causal, ws, out, dev_error=st.dev_error)
+
+    for i in range(2):
+        call(pools[i % len(pools)])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        call(pools[i % len(pools)])
+        b.record()
+    torch.cuda.synchronize()
+    assert int(st.dev_error.item()) == 0
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg = float(np.mean(ms))
+    rows = int(sum(-(-int(L) // 64) * 64 for L in inp.kv_lens))
+    flops = (2 * rows * d.d_latent * (d.d_nope + d.d_v) * d.num_heads
+             + 2 * d.num_heads * (d.d_nope + d.d_rope + d.d_v) * pairs)
+    tfs = flops / (avg * 1e-3) / 1e12
+    del ws, out
+    return {"call_us": avg * 1e3, "p50_us": float(np.median(ms)) * 1e3, "calls": calls,
+            "algorithmic_flops": int(flops), "mfma_tfs": tfs,
+            "mfma_frac": tfs / MFMA_BF16_PEAK_TFS, "bound": "mfma"}
 
 
 COPY_BYTES = 1 << 30
@@ -565,6 +611,10 @@ def main() -> int:
             log(f"[bench]   {w}: {rec['workloads'][w]['decode_us']:.1f} us, "
                 f"{rec['workloads'][w]['hbm_frac']*100:.1f} % HBM, "
                 f"{rec['workloads'][w]['mfma_frac']*100:.1f} % MFMA")
+            if "decompressed" in rec["workloads"][w]:
+                dc = rec["workloads"][w]["decompressed"]
+                log(f"[bench]   {w} non-absorbed: {dc['call_us']:.1f} us, "
+                    f"{dc['mfma_frac']*100:.1f} % MFMA")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")
         rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)

@@ -28,7 +28,8 @@ DEVERR_POSITION, DEVERR_SEQ, DEVERR_BLOCK, DEVERR_LENGTH = 1, 2, 4, 8
 EXPORTS = ["mla_status_string", "mla_rope_table", "mla_absorb_q", "mla_append_cache",
            "mla_decode_workspace_size", "mla_decode", "mla_out_proj", "mla_decode_noalloc",
            "mla_kv_down_workspace_size", "mla_kv_down_append", "mla_absorb_q_fused",
-           "mla_out_proj_fused_workspace_size", "mla_out_proj_fused"]
+           "mla_out_proj_fused_workspace_size", "mla_out_proj_fused",
+           "mla_prefill_workspace_size", "mla_prefill_decompressed"]
 
 
 class MlaError(RuntimeError):
@@ -76,6 +77,11 @@ def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mla_out_proj_fused_workspace_size.argtypes = [C, I32, I32, ctypes.POINTER(SZ)]
     lib.mla_out_proj_fused.restype = I32
     lib.mla_out_proj_fused.argtypes = [C, I32, I32, P, P, P, P, SZ, P]
+    lib.mla_prefill_workspace_size.restype = I32
+    lib.mla_prefill_workspace_size.argtypes = [C, I32, P, P, ctypes.POINTER(SZ)]
+    lib.mla_prefill_decompressed.restype = I32
+    lib.mla_prefill_decompressed.argtypes = [C, I32, P, P, P, P, P, I32, I64, P, P, P, P, P, I32,
+                                             P, SZ, P, P, P]
     lib.mla_kv_down_workspace_size.restype = I32
     lib.mla_kv_down_workspace_size.argtypes = [C, I32, I32, ctypes.POINTER(SZ)]
     lib.mla_kv_down_append.restype = I32
@@ -241,3 +247,29 @@ def out_proj_fused(cfg: MlaConfig, o_lat, w_ov, out, workspace, stream=None) -> 
     _check("mla_out_proj_fused", lib.mla_out_proj_fused(
         ctypes.byref(cfg), T, d_model, _ptr(o_lat), _ptr(w_ov), _ptr(out), _ptr(workspace),
         ws_bytes, _stream(stream)))
+
+
+def prefill_workspace_size(cfg: MlaConfig, q_start_host: np.ndarray,
+                           kv_lens_host: np.ndarray) -> int:
+    lib = load()
+    qs = np.ascontiguousarray(q_start_host, np.int32)
+    kl = np.ascontiguousarray(kv_lens_host, np.int32)
+    out = ctypes.c_size_t(0)
+    _check("mla_prefill_workspace_size", lib.mla_prefill_workspace_size(
+        ctypes.byref(cfg), len(kl), qs.ctypes.data, kl.ctypes.data, ctypes.byref(out)))
+    return out.value
+
+
+def prefill_decompressed(cfg: MlaConfig, q_start, kv_lens, q_start_host: np.ndarray,
+                         kv_lens_host: np.ndarray, block_table, num_pool_blocks: int, q_nope,
+                         q_lat, kv_pool, w_uk, w_uv, causal: bool, workspace, out,
+                         dev_error=None, stream=None) -> None:
+    lib = load()
+    qs = np.ascontiguousarray(q_start_host, np.int32)
+    kl = np.ascontiguousarray(kv_lens_host, np.int32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_prefill_decompressed", lib.mla_prefill_decompressed(
+        ctypes.byref(cfg), len(kl), _ptr(q_start), _ptr(kv_lens), qs.ctypes.data,
+        kl.ctypes.data, _ptr(block_table), block_table.shape[1], num_pool_blocks, _ptr(q_nope),
+        _ptr(q_lat), _ptr(kv_pool), _ptr(w_uk), _ptr(w_uv), int(causal), _ptr(workspace),
+        ws_bytes, _ptr(out), _ptr(dev_error), _stream(stream)))

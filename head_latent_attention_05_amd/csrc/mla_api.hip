@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "mla_internal.h"
@@ -371,6 +372,77 @@ mla_status mla_out_proj_fused(const mla_config* cfg, int32_t T, int32_t d_model,
     return MLA_ERR_WORKSPACE;
   return from_hip(
       launch_out_proj_fused(T, d_model, o_lat, w_ov, out, workspace, (hipStream_t)stream));
+}
+
+struct PrefillPlan {
+  int32_t T = 0;
+  int64_t R = 0;
+  int32_t max_qt = 0;
+};
+
+static mla_status plan_prefill(const mla_config* cfg, int32_t B, const int32_t* qs,
+                               const int32_t* kl, int32_t max_blocks, PrefillPlan* pp) {
+  mla_status s = check_cfg(cfg);
+  if (s != MLA_OK) return s;
+  if (!is_v3_bf16(*cfg)) return MLA_ERR_UNSUPPORTED;
+  if (B < 1 || !qs || !kl || qs[0] != 0) return MLA_ERR_INVALID_ARG;
+  int64_t R = 0;
+  int32_t max_qt = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t q = (int64_t)qs[b + 1] - qs[b];
+    const int64_t L = kl[b];
+    if (q < 0 || L < 1 || q > L) return MLA_ERR_INVALID_ARG;
+    const int64_t nblk = (L + 63) / 64;
+    if (max_blocks > 0 && nblk > max_blocks) return MLA_ERR_INVALID_ARG;
+    R += 64 * nblk;
+    max_qt = std::max<int32_t>(max_qt, (int32_t)((q + 63) / 64));  // 64-query tiles
+  }
+  if (R >= ((int64_t)1 << 31) || (int64_t)B * max_qt >= ((int64_t)1 << 31))
+    return MLA_ERR_UNSUPPORTED;
+  pp->T = qs[B];
+  pp->R = R;
+  pp->max_qt = max_qt;
+  return MLA_OK;
+}
+
+mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t num_seqs,
+                                      const int32_t* q_start_host,
+                                      const int32_t* kv_lens_host, size_t* bytes) {
+  PrefillPlan pp;
+  mla_status s = plan_prefill(cfg, num_seqs, q_start_host, kv_lens_host, 0, &pp);
+  if (s != MLA_OK) return s;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  *bytes = prefill_workspace_bytes(num_seqs, pp.R);
+  return MLA_OK;
+}
+
+mla_status mla_prefill_decompressed(const mla_config* cfg, int32_t num_seqs,
+                                    const int32_t* q_start, const int32_t* kv_lens,
+                                    const int32_t* q_start_host, const int32_t* kv_lens_host,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    int64_t num_pool_blocks, const void* q_nope,
+                                    const void* q_lat, const void* kv_pool, const void* w_uk,
+                                    const void* w_uv, int32_t causal, void* workspace,
+                                    size_t workspace_bytes, float* out, uint32_t* dev_error,
+                                    void* stream) {
+  if (max_blocks_per_seq < 1 || num_pool_blocks < 1) return MLA_ERR_INVALID_ARG;
+  PrefillPlan pp;
+  mla_status s = plan_prefill(cfg, num_seqs, q_start_host, kv_lens_host, max_blocks_per_seq, &pp);
+  if (s != MLA_OK) return s;
+  if (pp.T == 0) return MLA_OK;
+  if (!q_start || !kv_lens || !block_table || !q_nope || !q_lat || !kv_pool || !w_uk || !w_uv ||
+      !out)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(q_lat) || !aligned16(kv_pool) || !aligned16(w_uk) ||
+      !aligned16(w_uv) || !aligned16(out))
+    return MLA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < prefill_workspace_bytes(num_seqs, pp.R) ||
+      !aligned16(workspace))
+    return MLA_ERR_WORKSPACE;
+  return from_hip(launch_prefill(num_seqs, pp.T, pp.R, pp.max_qt, q_start, kv_lens, block_table,
+                                 max_blocks_per_seq, num_pool_blocks, q_nope, q_lat, kv_pool,
+                                 w_uk, w_uv, causal ? 1 : 0, cfg->softmax_scale, workspace, out,
+                                 dev_error, (hipStream_t)stream));
 }
 
 static mla_status check_kv_down(const mla_config* cfg, int32_t T, int32_t d_model) {

@@ -103,6 +103,13 @@ hipError_t launch_append(const mla_config& c, int T, const void* c_kv, const voi
                          const int32_t* bt, int num_seqs, int max_blocks, int64_t num_blocks,
                          const float* cos, const float* sin, int max_pos, void* pool,
                          void* q_lat, uint32_t* err, hipStream_t st);
+size_t prefill_workspace_bytes(int B, int64_t R);
+hipError_t launch_prefill(int B, int T, int64_t R, int max_qt, const int32_t* q_start,
+                          const int32_t* kv_lens, const int32_t* bt, int max_blocks,
+                          int64_t num_blocks, const void* q_nope, const void* q_lat,
+                          const void* pool, const void* w_uk, const void* w_uv, int causal,
+                          float scale, void* workspace, float* out, uint32_t* err,
+                          hipStream_t st);
 size_t out_fused_workspace_bytes(int T, int d_model);
 hipError_t launch_absorb_q_fused(int T, int d_cq, const void* c_q, const void* w_kq, void* q_lat,
                                  hipStream_t st);

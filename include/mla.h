@@ -254,6 +254,42 @@ mla_status mla_out_proj_fused(const mla_config* cfg, int32_t T, int32_t d_model,
                               size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Non-absorbed (explicit-decompression) attention, for prefill.
+ * --------------------------------------------------------------------------- */
+
+/* Workspace bytes for mla_prefill_decompressed: the per-head decompressed keys
+ * and values of every cached row of the batch (each sequence's rows rounded up
+ * to a multiple of 64): 2 * H * R * 128 * 2 bytes for R rounded rows, plus a
+ * small header.  Host arrays; the same length checks as the call. */
+mla_status mla_prefill_workspace_size(const mla_config* cfg, int32_t num_seqs,
+                                      const int32_t* q_start_host,
+                                      const int32_t* kv_lens_host, size_t* bytes);
+
+/* Attention with explicitly decompressed keys and values ([MLA explainer]
+ * forward_training: K_h = [W_UK_h c_kv | RoPE key], V_h = W_UV_h c_kv;
+ * [MLA architecture] 5.2: the form that suits prefill-heavy batches).  For query
+ * token t of sequence b at position P (as mla_decode) and every head h:
+ *   s_u = softmax_scale * ( sum_d q_nope[t][h][d] * K_h[u][d]
+ *                         + sum_i q_lat[t][h][d_latent + i] * row_u[d_latent + i] )
+ *   K_h[u][d] = round( sum_c w_uk[h][d][c] * row_u[c] ),  V_h[u][v] likewise with w_uv
+ *   out[t][h][v] = sum_u softmax(s)_u * V_h[u][v]    (fp32 out [T][H][d_v])
+ * over cached positions u < kv_lens[b] (u <= P when causal != 0).  The RoPE
+ * query columns come from q_lat (written by mla_append_cache); the same output
+ * as mla_absorb_q + mla_decode + mla_out_proj, up to rounding.  K_h and V_h are
+ * rounded to bf16 in the workspace (overwritten).  Other arguments as mla_decode.
+ * Only the DeepSeek-V3 bf16 configuration (UNSUPPORTED otherwise).  Device
+ * pointers, 16-byte aligned; WORKSPACE if the workspace is too small. */
+mla_status mla_prefill_decompressed(const mla_config* cfg, int32_t num_seqs,
+                                    const int32_t* q_start, const int32_t* kv_lens,
+                                    const int32_t* q_start_host, const int32_t* kv_lens_host,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    int64_t num_pool_blocks, const void* q_nope,
+                                    const void* q_lat, const void* kv_pool, const void* w_uk,
+                                    const void* w_uv, int32_t causal, void* workspace,
+                                    size_t workspace_bytes, float* out, uint32_t* dev_error,
+                                    void* stream);
+
+/* ---------------------------------------------------------------------------
  * Upstream of the cache: the joint KV down-projection fused with the append.
  * --------------------------------------------------------------------------- */
 

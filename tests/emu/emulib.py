@@ -126,6 +126,18 @@ class Emu:
             ctypes.byref(cfg), T, d_model, o_lat.ctypes.data, w_ov.ctypes.data, out.ctypes.data,
             ws.ctypes.data, ws.nbytes, None))
 
+    def prefill_decompressed(self, cfg, q_start, kv_lens, block_table, num_blocks, q_nope, q_lat,
+                             pool, w_uk, w_uv, causal, out, dev_error=None) -> None:
+        p = lambda a: None if a is None else a.ctypes.data
+        n = ctypes.c_size_t(0)
+        self.check("mla_prefill_workspace_size", self.lib.mla_prefill_workspace_size(
+            ctypes.byref(cfg), len(kv_lens), p(q_start), p(kv_lens), ctypes.byref(n)))
+        ws = self.empty((n.value,), np.uint8)
+        self.check("mla_prefill_decompressed", self.lib.mla_prefill_decompressed(
+            ctypes.byref(cfg), len(kv_lens), p(q_start), p(kv_lens), p(q_start), p(kv_lens),
+            p(block_table), block_table.shape[1], num_blocks, p(q_nope), p(q_lat), p(pool),
+            p(w_uk), p(w_uv), int(causal), p(ws), ws.nbytes, p(out), p(dev_error), None))
+
     def kv_down_workspace_size(self, cfg, T, d_model) -> int:
         out = ctypes.c_size_t(0)
         self.check("mla_kv_down_workspace_size", self.lib.mla_kv_down_workspace_size(

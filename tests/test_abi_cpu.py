@@ -248,3 +248,33 @@ def test_fused_weight_argument_checks():
     assert lib.mla_out_proj_fused(ctypes.byref(c), 4, 7168, F, F, F, None, 1 << 30, None) == 3
     assert lib.mla_out_proj_fused(ctypes.byref(c), 4, 7168, F, None, F, F, 1 << 30, None) == 1
     assert lib.mla_out_proj_fused(ctypes.byref(tiny), 4, 7168, F, F, F, F, 1 << 30, None) == 2
+
+
+def test_prefill_argument_checks():
+    lib = B.load()
+    c = B.MlaConfig.from_dims(synth.V3, 64)
+    tiny = B.MlaConfig.from_dims(synth.TINY, 64)
+    P = ctypes.c_void_p
+    F = P(FAKE)
+    qs = np.array([0, 3, 5], np.int32)
+    kl = np.array([100, 64], np.int32)
+    out = ctypes.c_size_t(0)
+    assert lib.mla_prefill_workspace_size(ctypes.byref(c), 2, qs.ctypes.data, kl.ctypes.data,
+                                          ctypes.byref(out)) == 0
+    R = 128 + 64   # each sequence's rows rounded up to a multiple of 64
+    assert out.value >= 2 * 128 * R * 128 * 2
+    assert lib.mla_prefill_workspace_size(ctypes.byref(tiny), 2, qs.ctypes.data, kl.ctypes.data,
+                                          ctypes.byref(out)) == 2
+    bad = np.array([0, 3, 80], np.int32)    # sequence 1: more queries than cached rows
+    assert lib.mla_prefill_workspace_size(ctypes.byref(c), 2, bad.ctypes.data, kl.ctypes.data,
+                                          ctypes.byref(out)) == 1
+
+    def call(ws_bytes=1 << 30, max_blocks=2, q_nope=FAKE):
+        return lib.mla_prefill_decompressed(
+            ctypes.byref(c), 2, F, F, P(qs.ctypes.data), P(kl.ctypes.data), F, max_blocks, 10,
+            P(q_nope), F, F, F, F, 1, F, ws_bytes, F, None, None)
+
+    assert call(max_blocks=1) == 1          # sequence 0 needs two 64-row blocks
+    assert call(q_nope=0) == 1
+    assert call(q_nope=FAKE + 4) == 1
+    assert call(ws_bytes=1024) == 3

@@ -383,3 +383,23 @@ def test_emu_fused_weight_projections(emu, T):
     emu.out_proj_fused(cfg, emu.put(fi.o_lat), emu.put(fi.w_ov), out)
     ref = O.out_proj_fused(d, O.storage_to_f64(fi.o_lat, d.dtype), fi.w_ov)
     assert np.abs(out - ref).max() <= 5e-5 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("name", ["v3_prefill_small", "v3_batch_ragged"])
+def test_emu_prefill_decompressed(emu, name):
+    """Non-absorbed attention (decompressed K and V) against the oracle's
+    explicit-decompression attention, causal chunked prefill and decode."""
+    inp = _inputs(**CASES[name])
+    d = inp.dims
+    st = EmuStep(emu, inp)
+    st.append()
+    out = emu.empty((inp.T, d.num_heads, d.d_v), np.float32)
+    emu.prefill_decompressed(st.cfg, st.q_start, st.kv_lens, st.block_table, st.num_blocks,
+                             st.q_nope, st.q_lat, st.pool, st.w_uk, st.w_uv,
+                             inp.workload.causal, out, st.dev_error)
+    assert int(st.dev_error[0]) == 0
+    pool = oracle_pool(inp)
+    heads = sample_heads(d.num_heads, 6)
+    ref = O.naive_mla(d, inp.w_uk, inp.w_uv, inp.q_nope, inp.q_pe, rows_fn(pool, inp),
+                      inp.kv_lens, inp.q_start, inp.workload.causal, heads)
+    check_out(d, out[:, heads], ref, f"emu prefill {name}")
