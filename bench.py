@@ -36,11 +36,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Sources of the decode call (its kernels, their launch and split plan): the
+# committed counters stay valid while none of these changes.
+DECODE_SOURCES = ("decode_v4.hip", "merge_v3.hip", "plan_device.h", "gfx950_asm.h",
+                  "uniform_ptr.h", "mla_internal.h", "mla_api.hip")
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "head_latent_attention_05_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + f.read())
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "head_latent_attention_05_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
