@@ -36,6 +36,10 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a, int H
   const int nlat = dc >> 6;
   const int64_t w = blockIdx.x;
   const PlanArgs& p = a.plan;
+  if (!plan_consistent(p, a.max_blocks)) {  // device lengths disagree with the host plan
+    if (w == 0 && blockIdx.y == 0 && threadIdx.x == 0 && a.err) atomicOr(a.err, MLA_DEVERR_LENGTH);
+    return;
+  }
   const int64_t u0 = range_start(w, p.U, p.G), u1 = range_start(w + 1, p.U, p.G);
   if (u0 >= u1) return;
   const S* pool = (const S*)a.pool;
@@ -120,7 +124,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a, int H, int dc)
   const int j = t - p.q_start[b];
   const int64_t ts = units_before_seq(p, b) + seq_units_before(L, q, j, p.block_size, p.causal);
   const int64_t nu = (attend_len(L, q, j, p.causal) + p.block_size - 1) / p.block_size;
-  const int64_t wlo = range_of(ts, p.U, p.G), whi = range_of(ts + nu - 1, p.U, p.G);
+  // ranges clamped to [0, G): device lengths that disagree with the host's (the
+  // decode kernel flags that) must not take a slot index out of the workspace
+  const int64_t whi = max<int64_t>(0, min<int64_t>(range_of((int64_t)ts + nu - 1, p.U, p.G), p.G - 1));
+  const int64_t wlo = max<int64_t>(0, min<int64_t>(range_of(ts, p.U, p.G), whi));
   if (wlo == whi) return;  // finished in place by one workgroup
   const int nlat = dc >> 6;
   float mx = -INFINITY;

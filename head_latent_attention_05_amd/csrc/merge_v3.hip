@@ -46,7 +46,10 @@ __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* 
   const int f0 = (tid & 15) * 32;
   int ts, nu;
   locate_token(p, t, ts, nu);
-  const int64_t wlo = range_of(ts, p.U, p.G), whi = range_of((int64_t)ts + nu - 1, p.U, p.G);
+  // ranges clamped to [0, G): device lengths that disagree with the host's (the
+  // decode kernel flags that) must not take a slot index out of the workspace
+  const int64_t whi = max<int64_t>(0, min<int64_t>(range_of((int64_t)ts + nu - 1, p.U, p.G), p.G - 1));
+  const int64_t wlo = max<int64_t>(0, min<int64_t>(range_of(ts, p.U, p.G), whi));
   if (wlo == whi) return;  // finished in place by one workgroup
   const int64_t slot_lo = range_start(wlo, p.U, p.G) == ts ? 2 * wlo : 2 * wlo + 1;
 

@@ -404,3 +404,52 @@ def test_emu_prefill_decompressed(emu, name):
     ref = O.naive_mla(d, inp.w_uk, inp.w_uv, inp.q_nope, inp.q_pe, rows_fn(pool, inp),
                       inp.kv_lens, inp.q_start, inp.workload.causal, heads)
     check_out(d, out[:, heads], ref, f"emu prefill {name}")
+
+
+@pytest.mark.parametrize("name", ["tiny_prefill", "v3_batch_ragged"])
+def test_emu_device_lengths_disagreeing_with_host_are_flagged(emu, name):
+    """The split plan comes from the host copies of the lengths; device copies
+    that disagree are flagged (MLA_DEVERR_LENGTH) and nothing outside the given
+    buffers is touched (every buffer ends at a guard page)."""
+    import ctypes
+    inp = _inputs(**CASES[name])
+    st = EmuStep(emu, inp)
+    st.append()
+    bad = emu.put(np.asarray(inp.kv_lens, np.int32) + 100)
+    qs = np.ascontiguousarray(inp.q_start, np.int32)
+    kl = np.ascontiguousarray(inp.kv_lens, np.int32)
+    st.dev_error[0] = 0
+    p = lambda a: None if a is None else a.ctypes.data
+    for G in (0, 7):
+        nbytes = emu.workspace_size(st.cfg, qs, kl, inp.workload.causal, G)
+        ws = emu.empty((max(nbytes, 16),), np.uint8)
+        rc = emu.lib.mla_decode(
+            ctypes.byref(st.cfg), len(kl), p(st.q_start), p(bad), qs.ctypes.data, kl.ctypes.data,
+            p(st.block_table), st.block_table.shape[1], st.num_blocks, p(st.q_lat), p(st.pool),
+            int(inp.workload.causal), G, p(ws), nbytes, p(st.o_lat), p(st.dev_error), None)
+        assert rc == 0
+        assert int(st.dev_error[0]) & B.DEVERR_LENGTH
+
+
+def test_emu_prefill_device_lengths_disagreeing_with_host_are_flagged(emu):
+    import ctypes
+    inp = _inputs(**CASES["v3_prefill_small"])
+    d = inp.dims
+    st = EmuStep(emu, inp)
+    st.append()
+    bad = emu.put(np.asarray(inp.kv_lens, np.int32) + 100)
+    qs = np.ascontiguousarray(inp.q_start, np.int32)
+    kl = np.ascontiguousarray(inp.kv_lens, np.int32)
+    p = lambda a: None if a is None else a.ctypes.data
+    n = ctypes.c_size_t(0)
+    assert emu.lib.mla_prefill_workspace_size(ctypes.byref(st.cfg), len(kl), qs.ctypes.data,
+                                              kl.ctypes.data, ctypes.byref(n)) == 0
+    ws = emu.empty((n.value,), np.uint8)
+    out = emu.empty((inp.T, d.num_heads, d.d_v), np.float32)
+    st.dev_error[0] = 0
+    rc = emu.lib.mla_prefill_decompressed(
+        ctypes.byref(st.cfg), len(kl), p(st.q_start), p(bad), qs.ctypes.data, kl.ctypes.data,
+        p(st.block_table), st.block_table.shape[1], st.num_blocks, p(st.q_nope), p(st.q_lat),
+        p(st.pool), p(st.w_uk), p(st.w_uv), 1, p(ws), ws.nbytes, p(out), p(st.dev_error), None)
+    assert rc == 0
+    assert int(st.dev_error[0]) & B.DEVERR_LENGTH
