@@ -5,13 +5,17 @@
 // an output normalised over that range's rows and the log2-sum-exp of its
 // scaled scores.  The softmax over all rows is the lse-weighted mix:
 //   o = sum_w 2^(lse_w - M) o_w / sum_w 2^(lse_w - M),   M = max_w lse_w,
-// taken in increasing w, so results are deterministic for a split plan.  This
+// taken in a fixed order, so results are deterministic for a split plan.  This
 // is the online-softmax identity that [MLA explainer] stage 2B's softmax
 // reduces to when its rows are processed in pieces.
 //
-// Workgroup = one token x 16 heads; thread = one head x 32 features (four
-// 16-byte loads per range, four ranges' loads in flight together).  The
-// token's unit range comes from one wave-parallel pass over the sequences.
+// Workgroup = one token x 4 heads, 4 waves; wave rg is range group rg, and a
+// lane owns one head x 32 features.  Group rg takes ranges wlo + rg, wlo + rg
+// + 4, ..., four per round with all their loads in flight (so a token split over
+// up to 16 ranges costs one round trip), combining rounds online; the four
+// groups' (maximum, denominator, weighted sum) meet in LDS and are combined in
+// increasing rg.  The token's unit range comes from one wave-parallel pass over
+// the sequences.
 #include <math.h>
 
 #include "plan_device.h"
@@ -22,6 +26,8 @@ namespace {
 constexpr int kH = 128;
 constexpr int kDC = 512;
 constexpr int kBS = 64;
+constexpr int kHG = 4;  // heads per workgroup
+constexpr int kRG = 4;  // range groups (one wave each)
 
 // Partial slot of range w for a token whose first unit is ts, among the ranges
 // wlo..whi that touch it: a range after wlo starts inside the token, so the
@@ -39,11 +45,15 @@ __device__ __forceinline__ void load4(const uint16_t* p, u32x4* x) {
 __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* __restrict__ ws_lse,
                                                        const uint16_t* __restrict__ ws_o,
                                                        uint16_t* __restrict__ o_lat) {
+  __shared__ float st_m[kRG][64];     // per range group: running maximum,
+  __shared__ float st_d[kRG][64];     // denominator
+  __shared__ f32x4 st_a[kRG][8][64];  // and weighted sum of 32 features
   p.block_size = kBS;  // a compile-time block size turns the unit arithmetic into shifts
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  const int h = blockIdx.y * 16 + (tid >> 4);
-  const int f0 = (tid & 15) * 32;
+  const int rg = tid >> 6, lane = tid & 63;
+  const int h = blockIdx.y * kHG + (lane >> 4);
+  const int f0 = (lane & 15) * 32;
   int ts, nu;
   locate_token(p, t, ts, nu);
   // ranges clamped to [0, G): device lengths that disagree with the host's (the
@@ -53,33 +63,33 @@ __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* 
   if (wlo == whi) return;  // finished in place by one workgroup
   const int64_t slot_lo = range_start(wlo, p.U, p.G) == ts ? 2 * wlo : 2 * wlo + 1;
 
-  // Ranges are taken four at a time with branch-free loads (indices past the
-  // last range repeat it and get weight 0), so a token's partials are all in
-  // flight together for up to four ranges.
-  float mx = -INFINITY;
-  for (int64_t w = wlo; w <= whi; w += 4) {
-    float l[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) l[j] = ws_lse[slot_of(min(w + j, whi), wlo, slot_lo) * kH + h];
-    mx = fmaxf(mx, fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])));
-  }
-
+  // Range group rg takes ranges wlo + rg + kRG*j, four per round with
+  // branch-free loads (indices past the last range repeat it and get weight 0),
+  // combining rounds online: running maximum, earlier sums rescaled when it grows.
+  float mx = -INFINITY, den = 0.f;
   float acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-  float den = 0.f;
-  for (int64_t w = wlo; w <= whi; w += 4) {
+  for (int64_t w0 = wlo + rg; w0 <= whi; w0 += 4 * kRG) {
     u32x4 x[4][4];
     float l[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t slot = slot_of(min(w + j, whi), wlo, slot_lo);
+      const int64_t slot = slot_of(min(w0 + kRG * j, whi), wlo, slot_lo);
       load4(ws_o + (slot * kH + h) * kDC + f0, x[j]);
       l[j] = ws_lse[slot * kH + h];
     }
 #pragma unroll
+    for (int j = 1; j < 4; ++j) l[j] = w0 + kRG * j <= whi ? l[j] : -INFINITY;
+    const float mn = fmaxf(mx, fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])));
+    const float sc = exp2f(mx - mn);  // 0 in the first round (mx = -inf, mn finite)
+    den *= sc;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] *= sc;
+    mx = mn;
+#pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float e = w + j <= whi ? exp2f(l[j] - mx) : 0.f;
+      const float e = exp2f(l[j] - mx);
       den += e;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -90,20 +100,42 @@ __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* 
         }
     }
   }
-  const float inv = 1.f / den;
+  // a group without ranges keeps (-inf, 0, 0), which adds nothing below
+  st_m[rg][lane] = mx;
+  st_d[rg][lane] = den;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    st_a[rg][i][lane] = f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+  __syncthreads();
+  if (rg != 0) return;
+  float M = st_m[0][lane];  // group 0 always holds range wlo: finite
+#pragma unroll
+  for (int r = 1; r < kRG; ++r) M = fmaxf(M, st_m[r][lane]);
+  float D = 0.f;
+  f32x4 A[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) A[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < kRG; ++r) {
+    const float e = exp2f(st_m[r][lane] - M);
+    D += e * st_d[r][lane];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A[i] += e * st_a[r][i][lane];
+  }
+  const float inv = 1.f / D;
   u32x4* dst = (u32x4*)(o_lat + ((int64_t)t * kH + h) * kDC + f0);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    dst[i] = u32x4{pack_bf16x2(acc[8 * i] * inv, acc[8 * i + 1] * inv),
-                   pack_bf16x2(acc[8 * i + 2] * inv, acc[8 * i + 3] * inv),
-                   pack_bf16x2(acc[8 * i + 4] * inv, acc[8 * i + 5] * inv),
-                   pack_bf16x2(acc[8 * i + 6] * inv, acc[8 * i + 7] * inv)};
+    dst[i] = u32x4{pack_bf16x2(A[2 * i][0] * inv, A[2 * i][1] * inv),
+                   pack_bf16x2(A[2 * i][2] * inv, A[2 * i][3] * inv),
+                   pack_bf16x2(A[2 * i + 1][0] * inv, A[2 * i + 1][1] * inv),
+                   pack_bf16x2(A[2 * i + 1][2] * inv, A[2 * i + 1][3] * inv)};
 }
 
 }  // namespace
 
 hipError_t launch_merge_v3(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(merge_v3_kernel, dim3(a.plan.T, kH / 16), dim3(256), 0, st, a.plan,
+  hipLaunchKernelGGL(merge_v3_kernel, dim3(a.plan.T, kH / kHG), dim3(256), 0, st, a.plan,
                      a.ws_lse, (const uint16_t*)a.ws_o, (uint16_t*)a.o_lat);
   return hipGetLastError();
 }
