@@ -395,7 +395,7 @@ static mla_status plan_prefill(const mla_config* cfg, int32_t B, const int32_t* 
     const int64_t nblk = (L + 63) / 64;
     if (max_blocks > 0 && nblk > max_blocks) return MLA_ERR_INVALID_ARG;
     R += 64 * nblk;
-    max_qt = std::max<int32_t>(max_qt, (int32_t)((q + 63) / 64));  // 64-query tiles
+    max_qt = std::max<int32_t>(max_qt, (int32_t)((q + 127) / 128));  // 128-query tiles
   }
   if (R >= ((int64_t)1 << 31) || (int64_t)B * max_qt >= ((int64_t)1 << 31))
     return MLA_ERR_UNSUPPORTED;

@@ -26,8 +26,8 @@
 //   one it multiplies: C^T[d][row] =
 //   W[d][.] . c_kv[row][.] on v_mfma_f32_16x16x32_bf16, 4 d-values per lane
 //   stored as 8 bytes.
-// attn_kernel: workgroup = (64 queries of one sequence, head), 4 waves x 16
-//   queries.  Key tiles of 64 rows ([K_nope | RoPE key] 400-byte LDS rows, V
+// attn_kernel: workgroup = (128 queries of one sequence, head), 8 waves x 16
+//   queries (two per SIMD, sharing every staged tile).  Key tiles of 64 rows ([K_nope | RoPE key] 400-byte LDS rows, V
 //   288-byte rows) are loaded into registers one tile ahead and staged in LDS.
 //   Per tile and wave: S^T[64 keys x 16 queries] = K . Q^T (24 MFMAs, Q^T in
 //   registers), online softmax per query (a lane owns one query and 16 keys,
@@ -50,7 +50,7 @@ constexpr int kDC = 512;
 constexpr int kRow = 576;
 constexpr int kDN = 128;              // no-RoPE query / key width (and value width)
 constexpr int kBS = 64;
-constexpr int kQT = 64;               // queries per attention workgroup (4 waves x 16)
+constexpr int kQT = 128;              // queries per attention workgroup (8 waves x 16)
 constexpr int kChunk = 4096;          // packed rows per decompression workgroup
 constexpr int kAhead = 2;             // 16-row blocks in flight ahead of the one multiplied
 constexpr int kWRowB = kDC * 2 + 16;  // W row in LDS (bytes, padded)
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
   if (bad && err) atomicOr(err, bad);
 }
 
-__global__ __launch_bounds__(256) void attn_kernel(
+__global__ __launch_bounds__(512) void attn_kernel(
     int B, int T, int max_qt, int64_t R, const int32_t* __restrict__ row_base,
     const int32_t* __restrict__ q_start, const int32_t* __restrict__ kv_lens,
     const int32_t* __restrict__ bt, int max_blocks, int64_t num_blocks,
@@ -242,23 +242,20 @@ __global__ __launch_bounds__(256) void attn_kernel(
   const int u_end = causal ? P0 + j0 + nq : L;
   const int ntiles = (u_end + kBS - 1) / kBS;
 
-  // tile loads per thread: 4 no-RoPE key, 2 RoPE key, 4 value pieces of 16 B
-  u32x4 kn[4], kr[2], vv[4];
+  // tile loads per thread: 2 no-RoPE key, 1 RoPE key, 2 value pieces of 16 B
+  u32x4 kn[2], kr, vv[2];
   const uint16_t* kd_h = kd + ((int64_t)h * R + rbase) * kDN;
   const uint16_t* vd_h = vd + ((int64_t)h * R + rbase) * kDN;
   auto load = [&](int k_t) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = tid + 256 * i, r = k >> 4, c = k & 15;
+    for (int i = 0; i < 2; ++i) {
+      const int k = tid + 512 * i, r = k >> 4, c = k & 15;
       kn[i] = *(const u32x4*)(kd_h + (int64_t)(kBS * k_t + r) * kDN + 8 * c);
       vv[i] = *(const u32x4*)(vd_h + (int64_t)(kBS * k_t + r) * kDN + 8 * c);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int k = tid + 256 * i, r = k >> 3, c = k & 7;
-      const int64_t row = key_row(bt, b, max_blocks, num_blocks, L, kBS * k_t + r, bad);
-      kr[i] = *(const u32x4*)(pool + row * kRow + kDC + 8 * c);
-    }
+    const int r = tid >> 3, c = tid & 7;
+    const int64_t row = key_row(bt, b, max_blocks, num_blocks, L, kBS * k_t + r, bad);
+    kr = *(const u32x4*)(pool + row * kRow + kDC + 8 * c);
   };
 
   float m_run = -INFINITY, l_part = 0.f;
@@ -269,16 +266,12 @@ __global__ __launch_bounds__(256) void attn_kernel(
   for (int k_t = 0; k_t < ntiles; ++k_t) {
     __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = tid + 256 * i, r = k >> 4, c = k & 15;
+    for (int i = 0; i < 2; ++i) {
+      const int k = tid + 512 * i, r = k >> 4, c = k & 15;
       *(u32x4*)(kt + r * kKRowB + 16 * c) = kn[i];
       *(u32x4*)(vt + r * kVRowB + 16 * c) = vv[i];
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int k = tid + 256 * i, r = k >> 3, c = k & 7;
-      *(u32x4*)(kt + r * kKRowB + 2 * kDN + 16 * c) = kr[i];
-    }
+    *(u32x4*)(kt + (tid >> 3) * kKRowB + 2 * kDN + 16 * (tid & 7)) = kr;
     __syncthreads();
     if (k_t + 1 < ntiles) load(k_t + 1);
 
@@ -381,7 +374,7 @@ hipError_t launch_prefill(int B, int T, int64_t R, int max_qt, const int32_t* q_
                      err);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_kernel, dim3(B * max_qt, kH), dim3(256), 0, st, B, T, max_qt, R, row_base,
+  hipLaunchKernelGGL(attn_kernel, dim3(B * max_qt, kH), dim3(512), 0, st, B, T, max_qt, R, row_base,
                      q_start, kv_lens, bt, max_blocks, num_blocks, (const uint16_t*)q_nope,
                      (const uint16_t*)q_lat, (const uint16_t*)pool, kd, vd, causal,
                      scale * kLog2e, out, err);
