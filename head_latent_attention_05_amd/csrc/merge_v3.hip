@@ -9,13 +9,14 @@
 // is the online-softmax identity that [MLA explainer] stage 2B's softmax
 // reduces to when its rows are processed in pieces.
 //
-// Workgroup = one token x 4 heads, 4 waves; wave rg is range group rg, and a
-// lane owns one head x 32 features.  Group rg takes ranges wlo + rg, wlo + rg
-// + 4, ..., four per round with all their loads in flight (so a token split over
-// up to 16 ranges costs one round trip), combining rounds online; the four
+// Workgroup = one token x 16/R heads in 4 waves, R = 1, 2 or 4 range groups:
+// wave v is range group v % R for head quad v / R, and a lane owns one head x 32
+// features.  Group rg takes ranges wlo + rg, wlo + rg + R, ..., four per round
+// with all their loads in flight, combining rounds online; with R > 1 the
 // groups' (maximum, denominator, weighted sum) meet in LDS and are combined in
-// increasing rg.  The token's unit range comes from one wave-parallel pass over
-// the sequences.
+// increasing rg.  R trades workgroups for round trips; the host picks it from
+// the most-split token and the token count.
+// The token's unit range comes from one wave-parallel pass over the sequences.
 #include <math.h>
 
 #include "plan_device.h"
@@ -26,8 +27,6 @@ namespace {
 constexpr int kH = 128;
 constexpr int kDC = 512;
 constexpr int kBS = 64;
-constexpr int kHG = 4;  // heads per workgroup
-constexpr int kRG = 4;  // range groups (one wave each)
 
 // Partial slot of range w for a token whose first unit is ts, among the ranges
 // wlo..whi that touch it: a range after wlo starts inside the token, so the
@@ -42,17 +41,22 @@ __device__ __forceinline__ void load4(const uint16_t* p, u32x4* x) {
   for (int i = 0; i < 4; ++i) x[i] = ((const u32x4*)p)[i];
 }
 
+template <int kRG>
 __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* __restrict__ ws_lse,
                                                        const uint16_t* __restrict__ ws_o,
                                                        uint16_t* __restrict__ o_lat) {
-  __shared__ float st_m[kRG][64];     // per range group: running maximum,
-  __shared__ float st_d[kRG][64];     // denominator
-  __shared__ f32x4 st_a[kRG][8][64];  // and weighted sum of 32 features
+  constexpr int kHG = 16 / kRG;  // heads per workgroup
+  constexpr int kSl = 256 / kRG;  // lanes of one range group
+  __shared__ float st_m[kRG][kSl];     // per range group: running maximum,
+  __shared__ float st_d[kRG][kSl];     // denominator
+  __shared__ f32x4 st_a[kRG][8][kSl];  // and weighted sum of 32 features
   p.block_size = kBS;  // a compile-time block size turns the unit arithmetic into shifts
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  const int rg = tid >> 6, lane = tid & 63;
-  const int h = blockIdx.y * kHG + (lane >> 4);
+  const int wave = tid >> 6, lane = tid & 63;
+  const int rg = wave % kRG, hq = wave / kRG;
+  const int sl = 64 * hq + lane;  // this lane's index within its range group
+  const int h = blockIdx.y * kHG + 4 * hq + (lane >> 4);
   const int f0 = (lane & 15) * 32;
   int ts, nu;
   locate_token(p, t, ts, nu);
@@ -100,27 +104,34 @@ __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* 
         }
     }
   }
-  // a group without ranges keeps (-inf, 0, 0), which adds nothing below
-  st_m[rg][lane] = mx;
-  st_d[rg][lane] = den;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    st_a[rg][i][lane] = f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
-  __syncthreads();
-  if (rg != 0) return;
-  float M = st_m[0][lane];  // group 0 always holds range wlo: finite
-#pragma unroll
-  for (int r = 1; r < kRG; ++r) M = fmaxf(M, st_m[r][lane]);
-  float D = 0.f;
   f32x4 A[8];
+  float D;
+  if constexpr (kRG == 1) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) A[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 8; ++i) A[i] = f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+    D = den;
+  } else {
+    // a group without ranges keeps (-inf, 0, 0), which adds nothing below
+    st_m[rg][sl] = mx;
+    st_d[rg][sl] = den;
 #pragma unroll
-  for (int r = 0; r < kRG; ++r) {
-    const float e = exp2f(st_m[r][lane] - M);
-    D += e * st_d[r][lane];
+    for (int i = 0; i < 8; ++i)
+      st_a[rg][i][sl] = f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+    __syncthreads();
+    if (rg != 0) return;
+    float M = st_m[0][sl];  // group 0 always holds range wlo: finite
 #pragma unroll
-    for (int i = 0; i < 8; ++i) A[i] += e * st_a[r][i][lane];
+    for (int r = 1; r < kRG; ++r) M = fmaxf(M, st_m[r][sl]);
+    D = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < kRG; ++r) {
+      const float e = exp2f(st_m[r][sl] - M);
+      D += e * st_d[r][sl];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) A[i] += e * st_a[r][i][sl];
+    }
   }
   const float inv = 1.f / D;
   u32x4* dst = (u32x4*)(o_lat + ((int64_t)t * kH + h) * kDC + f0);
@@ -135,8 +146,16 @@ __global__ __launch_bounds__(256) void merge_v3_kernel(PlanArgs p, const float* 
 }  // namespace
 
 hipError_t launch_merge_v3(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(merge_v3_kernel, dim3(a.plan.T, kH / kHG), dim3(256), 0, st, a.plan,
-                     a.ws_lse, (const uint16_t*)a.ws_o, (uint16_t*)a.o_lat);
+  const int rg = a.merge_groups;
+  const dim3 grid(a.plan.T, kH * rg / 16);
+  const uint16_t* ws_o = (const uint16_t*)a.ws_o;
+  uint16_t* o_lat = (uint16_t*)a.o_lat;
+  if (rg == 1)
+    hipLaunchKernelGGL(merge_v3_kernel<1>, grid, dim3(256), 0, st, a.plan, a.ws_lse, ws_o, o_lat);
+  else if (rg == 2)
+    hipLaunchKernelGGL(merge_v3_kernel<2>, grid, dim3(256), 0, st, a.plan, a.ws_lse, ws_o, o_lat);
+  else
+    hipLaunchKernelGGL(merge_v3_kernel<4>, grid, dim3(256), 0, st, a.plan, a.ws_lse, ws_o, o_lat);
   return hipGetLastError();
 }
 
