@@ -24,7 +24,10 @@
 // value product of tile i-1, and the other way round in the next phase.  Each
 // SIMD holds one wave of each team, so one wave's MFMAs overlap the other's
 // LDS reads and softmax, and the K reads of the score phase are spread over
-// both phases.  A workgroup barrier separates phases.
+// both phases.  A workgroup barrier separates phases.  The scoring wave runs at
+// a raised issue priority: its chain of LDS reads and MFMAs is the longer one,
+// and without it the SIMD favours the older wave, so team 1's score phases ran
+// longest.
 //
 // Tiles (half cache blocks, 32 rows, 36 KiB) stream HBM -> LDS with
 // direct-to-LDS loads (global_load_lds_dwordx4) into four buffers; every wave
@@ -517,8 +520,10 @@ __global__ __launch_bounds__(512, 1) void decode_v4_kernel(
       if (lg.valid) issue();  // tile i+2
       if (i > 0) value_phase(i - 1, d_prev, t_prev);
     } else if (has) {
+      __builtin_amdgcn_s_setprio(2);
       score_phase(i, d_i);
       advance();
+      __builtin_amdgcn_s_setprio(0);
     }
     // ---- phase 2i+1
     const int d_next = i + 1 < issued ? desc_of(i + 1) : 0;
@@ -529,8 +534,10 @@ __global__ __launch_bounds__(512, 1) void decode_v4_kernel(
       if (lg.valid) issue();  // tile i+3
       value_phase(i, d_i, t_i);
     } else {
+      __builtin_amdgcn_s_setprio(2);
       score_phase(i, d_i);
       advance();
+      __builtin_amdgcn_s_setprio(0);
     }
     d_prev = d_i;
     t_prev = t_i;

@@ -132,6 +132,7 @@ inline unsigned long long __ballot(int pred) {
 #define __builtin_amdgcn_s_waitcnt(x) ::emu::s_waitcnt(x)
 #define __builtin_amdgcn_sched_barrier(x) ((void)0)
 #define __builtin_amdgcn_sched_group_barrier(m, n, id) ((void)0)
+#define __builtin_amdgcn_s_setprio(x) ((void)0)
 // hardware transcendentals: the emulator uses the libm functions (the GPU's are
 // within about 1 ulp of them)
 #define __builtin_amdgcn_exp2f(x) exp2f(x)
