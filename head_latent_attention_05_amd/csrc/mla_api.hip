@@ -70,7 +70,6 @@ struct HostPlan {
   int32_t T = 0;
   int64_t U = 0;
   int32_t G = 0;
-  int64_t max_token_ranges = 0;  // KV ranges that one token's units can meet
   size_t ws_bytes = 0;
   size_t lse_bytes = 0;
 };
@@ -79,13 +78,12 @@ mla_status plan_decode(const mla_config& c, int32_t B, const int32_t* qs, const 
                        int32_t causal, int32_t num_wg, HostPlan* hp) {
   if (B < 1 || !qs || !kl || num_wg < 0) return MLA_ERR_INVALID_ARG;
   if (qs[0] != 0) return MLA_ERR_INVALID_ARG;
-  int64_t U = 0, umax = 0;
+  int64_t U = 0;
   for (int b = 0; b < B; ++b) {
     const int64_t q = (int64_t)qs[b + 1] - qs[b];
     const int64_t L = kl[b];
     if (q < 0 || L < 1 || q > L) return MLA_ERR_INVALID_ARG;
     U += seq_units_before(L, q, q, c.block_size, causal ? 1 : 0);
-    if (q > 0) umax = std::max<int64_t>(umax, (L + c.block_size - 1) / c.block_size);
   }
   if (U >= ((int64_t)1 << 31)) return MLA_ERR_UNSUPPORTED;  // unit indices are 32-bit
   hp->T = qs[B];
@@ -107,8 +105,6 @@ mla_status plan_decode(const mla_config& c, int32_t B, const int32_t* qs, const 
   if (G > U) G = U;
   if (G > (1 << 30)) G = 1 << 30;
   hp->G = (int32_t)G;
-  // ranges hold at least U/G units, so a run of umax units meets at most this many
-  hp->max_token_ranges = (umax - 1 + U / G - 1) / (U / G) + 1;
   if (G == 1) {
     hp->ws_bytes = 0;
     hp->lse_bytes = 0;
@@ -185,20 +181,6 @@ mla_status decode_planned(const mla_config* cfg, const HostPlan& hp, int32_t num
   a.ws_o = hp.ws_bytes ? (void*)((char*)workspace + hp.lse_bytes) : nullptr;
   a.err = dev_error;
   a.scale_log2 = cfg->softmax_scale * kLog2e;
-  a.merge_groups = 1;
-  if (hp.G > 1 && is_v3_bf16(*cfg)) {
-    // Merge range groups (1, 2 or 4) per token: more groups spread a token's
-    // ranges over more waves, but the grid is T x 8 x groups workgroups, and
-    // past about four per compute unit it no longer runs in one pass, which
-    // costs more than the extra rounds of loads.
-    int cus = 0;
-    mla_status s = device_cus(&cus);
-    if (s != MLA_OK) return s;
-    const int64_t nr = hp.max_token_ranges;
-    a.merge_groups = nr <= 4 ? 1 : nr <= 8 ? 2 : 4;
-    while (a.merge_groups > 1 && (int64_t)hp.T * 8 * a.merge_groups > 4 * (int64_t)cus)
-      a.merge_groups /= 2;
-  }
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (is_v3_bf16(*cfg) && v3_kernels_available())

@@ -139,7 +139,6 @@ struct DecodeArgs {
   void* ws_o;
   uint32_t* err;
   float scale_log2;  // softmax_scale * log2(e)
-  int32_t merge_groups;  // range groups per token in the V3 merge: 1, 2 or 4
 };
 hipError_t launch_decode_generic(const mla_config& c, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_v3(const DecodeArgs& a, hipStream_t st);

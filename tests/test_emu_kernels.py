@@ -119,15 +119,16 @@ def test_emu_decode_splits(emu, name):
     emu.set_seed(1)
 
 
-@pytest.mark.parametrize("kv_lens,G", [([1000], 100000), ([1000, 700], 100000), ([1000, 700], 7),
-                                       ([70, 129, 1, 64, 200], 100000),
-                                       ([1000, 700, 300, 500, 900], 100000)])
-def test_emu_merge_range_groups(emu, kv_lens, G):
-    """The V3 merge with 4, 2 and 1 range groups per token.  With 8 emulated
-    compute units: one token split over 16 ranges takes 4 groups; two such
-    tokens take 2 (the grid is kept within 4 workgroups per compute unit), as do
-    two tokens over 7 ranges; five tokens of at most 4 ranges take 1, and five
-    tokens of up to 16 ranges take 1 in four rounds of loads."""
+@pytest.mark.parametrize("kv_lens", [
+    [1000],                                   # one token over 16 ranges: 2 rounds of 8
+    [200, 100],                               # at most 4 ranges per token: 1 round
+    [1000] + [37 * k for k in range(1, 16)],  # 16 tokens of 1 to 16 ranges
+    [2000, 1500, 1, 64],                      # 32 ranges: 4 rounds
+])
+def test_emu_merge_rounds(emu, kv_lens):
+    """The V3 merge with each token split over one range per cache block: one
+    round of eight ranges, several rounds combined online, and tokens of one
+    block (finished in place) beside split ones."""
     inp = _inputs("batch64", kv_lens=kv_lens)
     d = inp.dims
     st = EmuStep(emu, inp)
@@ -138,7 +139,7 @@ def test_emu_merge_range_groups(emu, kv_lens, G):
     ref = O.latent_decode(d, O.storage_to_f64(q, d.dtype), rows_fn(oracle_pool(inp), inp),
                           inp.kv_lens, inp.q_start, inp.workload.causal, heads)
     st.o_lat[...] = 0
-    st.decode(G)
+    st.decode(100000)
     got = O.storage_to_f64(st.o_lat, d.dtype)
     assert np.abs(got[:, heads] - ref).max() <= 2.0 ** -7 * np.abs(ref).max()
 
