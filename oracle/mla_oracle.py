@@ -35,7 +35,10 @@ plus the relative-position property of the scores; the weight-level
 absorption by brute-force loops and its associativity with the per-head
 calls; kv_down by brute-force
 scalar loops, one-hot inputs and closed forms of the normalisation, and the
-one-step bf16 rounding by constructed ties; none is "parity unpinned".
+one-step bf16 rounding by constructed ties; the e4m3 cache by torch's own
+float8_e4m3fn conversions, the format's closed-form values, constructed ties,
+and the rotated RoPE columns read back against an exact fp64 rotation at each
+token's true position; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -168,6 +171,97 @@ def gather_rows(pool: np.ndarray, dims, block_size: int, block_table: np.ndarray
     idx = [slot_of(block_table, seq, p, block_size) for p in range(length)]
     return storage_to_f64(pool[idx], dims.dtype)
 
+
+
+# ----------------------------------------------------------------------------
+# fp8 (e4m3) latent cache  ([MLA architecture] 4.2, "量化的影响": a quantised
+# cache halves the bytes per cached token, at a cost in numerical stability).
+# Reading (the pages leave the format open): rows are stored as OCP e4m3
+# (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; subnormals down to
+# 2^-9; largest finite 448; 0x7F / 0xFF are NaN).  One power-of-two scale per
+# cache: code = e4m3(x / kv_scale), value = kv_scale * decode(code).  Encoding
+# rounds to nearest, ties to even, and saturates finite values at +-448.
+# ----------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+E4M3_SENTINEL = 0x7F  # NaN: marks pool slots that were never written
+
+
+def e4m3_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Value of each e4m3 code (uint8) in fp64; NaN codes give NaN."""
+    b = np.asarray(bits, np.uint8).astype(np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -9), np.ldexp(8.0 + m, e - 10))
+    mag = np.where((e == 15) & ((b & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def f32_to_e4m3_bits(x32: np.ndarray) -> np.ndarray:
+    """fp32 -> e4m3 code: round to nearest, ties to even, |x| clamped to 448
+    first (saturation); NaN -> 0x7F.  The quantum is 2^(e-3) for a value in
+    [2^e, 2^(e+1)), e >= -6, and 2^-9 below 2^-6 (subnormals)."""
+    x = np.asarray(x32, np.float32).astype(np.float64)
+    nan = np.isnan(x)
+    x = np.where(nan, 0.0, x)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    _, ex = np.frexp(a)                      # a = f * 2^ex, 0.5 <= f < 1
+    e = np.maximum(ex - 1, -6)               # a in [2^e, 2^(e+1)) for normals
+    quantum = np.ldexp(1.0, e - 3)
+    q = np.rint(a / quantum) * quantum       # rint: half to even; exact in fp64
+    q = np.minimum(q, E4M3_MAX)
+    # encode q exactly
+    _, qx = np.frexp(q)
+    qe = np.maximum(qx - 1, -6)
+    normal = q >= 2.0 ** -6
+    mant = np.where(normal, q / np.ldexp(1.0, qe - 3) - 8.0, q / 2.0 ** -9)
+    code = np.where(normal, ((qe + 7) << 3) + mant.astype(np.int64), mant.astype(np.int64))
+    code = code.astype(np.int64) | np.where(neg & (q > 0), 0x80, 0)
+    code = np.where(neg & (q == 0), 0x80, code)   # keep the sign of zero
+    return np.where(nan, 0x7F, code).astype(np.uint8)
+
+
+def new_pool_fp8(num_blocks: int, block_size: int, row: int) -> np.ndarray:
+    """An e4m3 pool filled with the NaN sentinel 0x7F."""
+    return np.full((num_blocks * block_size, row), E4M3_SENTINEL, np.uint8)
+
+
+def append_cache_fp8(pool: np.ndarray, dims, block_size: int, seqs, positions,
+                     c_kv: np.ndarray, k_pe: np.ndarray, block_table: np.ndarray,
+                     cos32: np.ndarray, sin32: np.ndarray, kv_scale: float) -> None:
+    """The fp8 form of append_cache: the token's c_kv (bf16 input, exact in
+    fp32) and its RoPE-rotated k_pe (fp32, the same op order as the bf16 cache,
+    no intermediate bf16 rounding) are divided by the power-of-two kv_scale
+    (exact) and rounded once to e4m3."""
+    check_kv_scale(kv_scale)
+    dc = dims.d_latent
+    positions = np.asarray(positions)
+    slots = np.array([slot_of(block_table, int(b), int(p), block_size)
+                      for b, p in zip(seqs, positions)], dtype=np.int64)
+    if len(slots) == 0:
+        return
+    inv = np.float32(1.0 / kv_scale)
+    c32 = bf16_to_f64(c_kv).astype(np.float32)
+    x32 = bf16_to_f64(k_pe).astype(np.float32)
+    y32 = rope_cache_f32(x32, cos32[positions], sin32[positions])
+    pool[slots, :dc] = f32_to_e4m3_bits((c32 * inv).astype(np.float32))
+    pool[slots, dc:] = f32_to_e4m3_bits((y32 * inv).astype(np.float32))
+
+
+def check_kv_scale(kv_scale: float) -> None:
+    m, _ = math.frexp(float(kv_scale))
+    if not (kv_scale > 0 and m == 0.5 and 2.0 ** -60 <= kv_scale <= 2.0 ** 60):
+        raise ValueError("kv_scale must be a power of two in [2^-60, 2^60]")
+
+
+def gather_rows_fp8(pool: np.ndarray, dims, block_size: int, block_table: np.ndarray,
+                    seq: int, length: int, kv_scale: float) -> np.ndarray:
+    """Logical rows 0..length-1 of one sequence of an e4m3 pool, dequantised
+    to fp64: kv_scale * decode(code)."""
+    idx = [slot_of(block_table, seq, p, block_size) for p in range(length)]
+    return kv_scale * e4m3_to_f64(pool[idx])
 
 # ----------------------------------------------------------------------------
 # Attention
@@ -396,6 +490,37 @@ def build_pool(inp, block_size: int = 64, cos32=None, sin32=None,
         s, p, ck, kp = inp.new_tokens()
         append_cache(pool, d, block_size, s, p, ck, kp, inp.block_table, cos32, sin32)
     return pool
+
+
+def build_pool_fp8(inp, kv_scale: float, block_size: int = 64, cos32=None, sin32=None,
+                   which: str = "all") -> np.ndarray:
+    """build_pool for an e4m3 cache (bf16 inputs only)."""
+    d = inp.dims
+    if d.dtype != "bf16":
+        raise ValueError("the fp8 cache is built from bf16 inputs")
+    if cos32 is None:
+        cos32, sin32 = rope_table_f32(inp.max_pos(), d.d_rope)
+    pool = new_pool_fp8(inp.num_blocks, block_size, d.row)
+    if which in ("all", "history"):
+        s, p, ck, kp = inp.history()
+        append_cache_fp8(pool, d, block_size, s, p, ck, kp, inp.block_table, cos32, sin32,
+                         kv_scale)
+    if which == "all":
+        s, p, ck, kp = inp.new_tokens()
+        append_cache_fp8(pool, d, block_size, s, p, ck, kp, inp.block_table, cos32, sin32,
+                         kv_scale)
+    return pool
+
+
+def step_fp8(inp, kv_scale: float, heads: Optional[list] = None, block_size: int = 64):
+    """Full step over an e4m3 cache: append every token, then naive attention
+    over the dequantised rows.  Returns (out fp64 [T,H',d_v], pool)."""
+    pool = build_pool_fp8(inp, kv_scale, block_size)
+    rows = lambda b: gather_rows_fp8(pool, inp.dims, block_size, inp.block_table, b,
+                                     int(inp.kv_lens[b]), kv_scale)
+    out = naive_mla(inp.dims, inp.w_uk, inp.w_uv, inp.q_nope, inp.q_pe, rows,
+                    inp.kv_lens, inp.q_start, inp.workload.causal, heads)
+    return out, pool
 
 
 def step(inp, heads: Optional[list] = None, block_size: int = 64):
