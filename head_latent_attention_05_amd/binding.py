@@ -29,7 +29,8 @@ EXPORTS = ["mla_status_string", "mla_rope_table", "mla_absorb_q", "mla_append_ca
            "mla_decode_workspace_size", "mla_decode", "mla_out_proj", "mla_decode_noalloc",
            "mla_kv_down_workspace_size", "mla_kv_down_append", "mla_absorb_q_fused",
            "mla_out_proj_fused_workspace_size", "mla_out_proj_fused",
-           "mla_prefill_workspace_size", "mla_prefill_decompressed"]
+           "mla_prefill_workspace_size", "mla_prefill_decompressed", "mla_append_cache_fp8",
+           "mla_decode_fp8"]
 
 
 class MlaError(RuntimeError):
@@ -87,6 +88,12 @@ def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.mla_kv_down_append.restype = I32
     lib.mla_kv_down_append.argtypes = [C, I32, I32, P, P, P, P, ctypes.c_float, P, P, P, P, I32,
                                        I32, I64, P, P, I32, P, SZ, P, P, P, P]
+    lib.mla_append_cache_fp8.restype = I32
+    lib.mla_append_cache_fp8.argtypes = [C, I32, P, P, P, P, P, P, I32, I32, I64, P, P, I32,
+                                         ctypes.c_float, P, P, P, P]
+    lib.mla_decode_fp8.restype = I32
+    lib.mla_decode_fp8.argtypes = [C, I32, P, P, P, P, P, I32, I64, P, P, ctypes.c_float, I32,
+                                   I32, P, SZ, P, P, P]
     return lib
 
 
@@ -155,6 +162,18 @@ def append_cache(cfg: MlaConfig, c_kv, k_pe, q_pe, token_seq, positions, block_t
         _ptr(q_lat), _ptr(dev_error), _stream(stream)))
 
 
+def append_cache_fp8(cfg: MlaConfig, c_kv, k_pe, q_pe, token_seq, positions, block_table,
+                     num_pool_blocks: int, rope_cos, rope_sin, kv_scale: float, kv_pool,
+                     q_lat=None, dev_error=None, stream=None) -> None:
+    lib = load()
+    T = c_kv.shape[0]
+    _check("mla_append_cache_fp8", lib.mla_append_cache_fp8(
+        ctypes.byref(cfg), T, _ptr(c_kv), _ptr(k_pe), _ptr(q_pe), _ptr(token_seq),
+        _ptr(positions), _ptr(block_table), block_table.shape[0], block_table.shape[1],
+        num_pool_blocks, _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], kv_scale,
+        _ptr(kv_pool), _ptr(q_lat), _ptr(dev_error), _stream(stream)))
+
+
 def decode_workspace_size(cfg: MlaConfig, q_start_host: np.ndarray, kv_lens_host: np.ndarray,
                           causal: bool, num_workgroups: int = 0) -> int:
     lib = load()
@@ -179,6 +198,21 @@ def decode(cfg: MlaConfig, q_start, kv_lens, q_start_host: np.ndarray, kv_lens_h
         kl.ctypes.data, _ptr(block_table), block_table.shape[1], num_pool_blocks,
         _ptr(q_lat), _ptr(kv_pool), int(causal), num_workgroups, _ptr(workspace), ws_bytes,
         _ptr(o_lat), _ptr(dev_error), _stream(stream)))
+
+
+def decode_fp8(cfg: MlaConfig, q_start, kv_lens, q_start_host: np.ndarray,
+               kv_lens_host: np.ndarray, block_table, num_pool_blocks: int, q_lat, kv_pool,
+               kv_scale: float, causal: bool, o_lat, workspace=None, num_workgroups: int = 0,
+               dev_error=None, stream=None) -> None:
+    lib = load()
+    qs = np.ascontiguousarray(q_start_host, np.int32)
+    kl = np.ascontiguousarray(kv_lens_host, np.int32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mla_decode_fp8", lib.mla_decode_fp8(
+        ctypes.byref(cfg), len(kl), _ptr(q_start), _ptr(kv_lens), qs.ctypes.data,
+        kl.ctypes.data, _ptr(block_table), block_table.shape[1], num_pool_blocks,
+        _ptr(q_lat), _ptr(kv_pool), kv_scale, int(causal), num_workgroups, _ptr(workspace),
+        ws_bytes, _ptr(o_lat), _ptr(dev_error), _stream(stream)))
 
 
 def decode_noalloc(cfg: MlaConfig, q_start, kv_lens, q_start_host: np.ndarray,

@@ -117,6 +117,70 @@ __global__ __launch_bounds__(256) void append_v3_kernel(
   }
 }
 
+// e4m3 cache, DeepSeek-V3 shapes: part 0 writes the 576-byte row, c_kv (64
+// threads x 8 values) and the rotated k_pe (4 threads x 8 pairs), each value
+// multiplied by 1/kv_scale (a power of two, so exactly) and rounded once to e4m3;
+// parts 1 and 2 write the bf16 RoPE columns of q_lat exactly as append_v3_kernel.
+__global__ __launch_bounds__(256) void append_fp8_kernel(
+    const uint16_t* __restrict__ c_kv, const uint16_t* __restrict__ k_pe,
+    const uint16_t* __restrict__ q_pe, const int32_t* __restrict__ seq,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ bt, int num_seqs, int max_blocks,
+    int64_t num_blocks, const float* __restrict__ cosT, const float* __restrict__ sinT,
+    int max_pos, float inv_scale, uint8_t* __restrict__ pool, uint16_t* __restrict__ q_lat,
+    uint32_t* err) {
+  const int t = blockIdx.y, part = blockIdx.x, tid = threadIdx.x;
+  const int s = seq[t];
+  const int p = pos[t];
+  uint32_t bad = 0;
+  if (s < 0 || s >= num_seqs) bad |= MLA_DEVERR_SEQ;
+  if (p < 0 || p >= max_pos) bad |= MLA_DEVERR_POSITION;
+  int64_t blk = -1;
+  if (!bad) {
+    if (p / 64 >= max_blocks) {
+      bad |= MLA_DEVERR_POSITION;
+    } else {
+      blk = bt[(int64_t)s * max_blocks + p / 64];
+      if (blk < 0 || blk >= num_blocks) bad |= MLA_DEVERR_BLOCK;
+    }
+  }
+  if (bad) {
+    if (part == 0 && tid == 0 && err) atomicOr(err, bad);
+    return;
+  }
+  const float* cr = cosT + (int64_t)p * kV3Half;
+  const float* sr = sinT + (int64_t)p * kV3Half;
+  if (part > 0) {
+    const int h = 64 * (part - 1) + (tid >> 2), i0 = (tid & 3) * 8;
+    rope8_bf16(q_pe + ((int64_t)t * kV3H + h) * kV3Dr, cr, sr, i0,
+               q_lat + ((int64_t)t * kV3H + h) * kV3Row + kV3Dc);
+    return;
+  }
+  uint8_t* row = pool + (blk * 64 + p % 64) * (int64_t)kV3Row;
+  auto pack8 = [&](const float* v) {
+    u32x2 o = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma clang fp contract(off)
+      const float y = v[j] * inv_scale;
+      o[j >> 2] |= (uint32_t)f32_to_e4m3(y) << (8 * (j & 3));
+    }
+    return o;
+  };
+  if (tid < 64) {
+    const u32x4 c = *(const u32x4*)(c_kv + (int64_t)t * kV3Dc + 8 * tid);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = bf16_bits_to_f32((uint16_t)(c[j >> 1] >> (16 * (j & 1))));
+    *(u32x2*)(row + 8 * tid) = pack8(v);
+  } else if (tid < 68) {
+    const int i0 = (tid - 64) * 8;
+    float y1[8], y2[8];
+    rope8_pairs(k_pe + (int64_t)t * kV3Dr, cr, sr, i0, y1, y2);
+    *(u32x2*)(row + kV3Dc + i0) = pack8(y1);
+    *(u32x2*)(row + kV3Dc + kV3Half + i0) = pack8(y2);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(const mla_config& c, int T, const void* c_kv, const void* k_pe,
@@ -147,6 +211,18 @@ hipError_t launch_append(const mla_config& c, int T, const void* c_kv, const voi
         (const float*)q_pe, seq, pos, bt, num_seqs, max_blocks, num_blocks, cosT, sinT, max_pos,
         (float*)pool, (float*)q_lat, err);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_append_fp8(int T, const void* c_kv, const void* k_pe, const void* q_pe,
+                             const int32_t* seq, const int32_t* pos, const int32_t* bt,
+                             int num_seqs, int max_blocks, int64_t num_blocks, const float* cosT,
+                             const float* sinT, int max_pos, float inv_scale, void* pool,
+                             void* q_lat, uint32_t* err, hipStream_t st) {
+  hipLaunchKernelGGL(append_fp8_kernel, dim3(q_pe ? 3 : 1, T), dim3(256), 0, st,
+                     (const uint16_t*)c_kv, (const uint16_t*)k_pe, (const uint16_t*)q_pe, seq,
+                     pos, bt, num_seqs, max_blocks, num_blocks, cosT, sinT, max_pos, inv_scale,
+                     (uint8_t*)pool, (uint16_t*)q_lat, err);
   return hipGetLastError();
 }
 

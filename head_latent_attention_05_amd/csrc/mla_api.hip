@@ -30,6 +30,14 @@ bool is_f32_supported(const mla_config& c) {
          c.d_nope >= 1 && c.d_nope <= 256 && c.d_v >= 1 && c.d_v <= 256 && c.block_size == 64;
 }
 
+// kv_scale of an e4m3 cache: a power of two in [2^-60, 2^60]
+bool kv_scale_ok(float s) {
+  if (!(s > 0.f) || !isfinite(s)) return false;
+  int e = 0;
+  const float m = frexpf(s, &e);
+  return m == 0.5f && e >= -59 && e <= 61;
+}
+
 mla_status check_cfg(const mla_config* c) {
   if (!c) return MLA_ERR_INVALID_ARG;
   if (c->num_heads < 1 || c->d_latent < 1 || c->d_rope < 2 || (c->d_rope & 1) ||
@@ -147,7 +155,7 @@ mla_status decode_planned(const mla_config* cfg, const HostPlan& hp, int32_t num
                           int32_t max_blocks_per_seq, int64_t num_pool_blocks,
                           const void* q_lat, const void* kv_pool, int32_t causal,
                           void* workspace, bool use_scratch, void* o_lat, uint32_t* dev_error,
-                          void* stream) {
+                          void* stream, const float* kv_scale_fp8 = nullptr) {
   if (!q_start || !kv_lens || !block_table || !q_lat || !kv_pool || !o_lat)
     return MLA_ERR_INVALID_ARG;
   if (!aligned16(q_lat) || !aligned16(kv_pool) || !aligned16(o_lat)) return MLA_ERR_INVALID_ARG;
@@ -183,7 +191,9 @@ mla_status decode_planned(const mla_config* cfg, const HostPlan& hp, int32_t num
   a.scale_log2 = cfg->softmax_scale * kLog2e;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
-  if (is_v3_bf16(*cfg) && v3_kernels_available())
+  if (kv_scale_fp8)
+    e = launch_decode_fp8(a, *kv_scale_fp8, st);
+  else if (is_v3_bf16(*cfg) && v3_kernels_available())
     e = launch_decode_v3(a, st);
   else
     e = launch_decode_generic(*cfg, a, st);
@@ -494,6 +504,58 @@ mla_status mla_kv_down_append(const mla_config* cfg, int32_t T, int32_t d_model,
                                         max_blocks_per_seq, num_pool_blocks, rope_cos, rope_sin,
                                         max_pos, workspace, kv_pool, q_lat, dev_error,
                                         (hipStream_t)stream));
+}
+
+mla_status mla_append_cache_fp8(const mla_config* cfg, int32_t T, const void* c_kv,
+                                const void* k_pe, const void* q_pe, const int32_t* token_seq,
+                                const int32_t* positions, const int32_t* block_table,
+                                int32_t num_seqs, int32_t max_blocks_per_seq,
+                                int64_t num_pool_blocks, const float* rope_cos,
+                                const float* rope_sin, int32_t max_pos, float kv_scale,
+                                void* kv_pool, void* q_lat, uint32_t* dev_error, void* stream) {
+  mla_status s = check_cfg(cfg);
+  if (s != MLA_OK) return s;
+  if (!is_v3_bf16(*cfg)) return MLA_ERR_UNSUPPORTED;
+  if (!kv_scale_ok(kv_scale)) return MLA_ERR_INVALID_ARG;
+  if (T < 0) return MLA_ERR_INVALID_ARG;
+  if (T == 0) return MLA_OK;
+  if (!c_kv || !k_pe || !token_seq || !positions || !block_table || !rope_cos || !rope_sin ||
+      !kv_pool)
+    return MLA_ERR_INVALID_ARG;
+  if ((q_pe == nullptr) != (q_lat == nullptr)) return MLA_ERR_INVALID_ARG;
+  if (num_seqs < 1 || max_blocks_per_seq < 1 || num_pool_blocks < 1 || max_pos < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned16(c_kv) || !aligned16(k_pe) || !aligned16(kv_pool) || !aligned16(rope_cos) ||
+      !aligned16(rope_sin) || (q_pe && (!aligned16(q_pe) || !aligned16(q_lat))))
+    return MLA_ERR_INVALID_ARG;
+  return from_hip(launch_append_fp8(T, c_kv, k_pe, q_pe, token_seq, positions, block_table,
+                                    num_seqs, max_blocks_per_seq, num_pool_blocks, rope_cos,
+                                    rope_sin, max_pos, 1.0f / kv_scale, kv_pool, q_lat,
+                                    dev_error, (hipStream_t)stream));
+}
+
+mla_status mla_decode_fp8(const mla_config* cfg, int32_t num_seqs, const int32_t* q_start,
+                          const int32_t* kv_lens, const int32_t* q_start_host,
+                          const int32_t* kv_lens_host, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, int64_t num_pool_blocks, const void* q_lat,
+                          const void* kv_pool, float kv_scale, int32_t causal,
+                          int32_t num_workgroups, void* workspace, size_t workspace_bytes,
+                          void* o_lat, uint32_t* dev_error, void* stream) {
+  mla_status s = check_cfg(cfg);
+  if (s != MLA_OK) return s;
+  if (!is_v3_bf16(*cfg)) return MLA_ERR_UNSUPPORTED;
+  if (!kv_scale_ok(kv_scale)) return MLA_ERR_INVALID_ARG;
+  HostPlan hp;
+  s = plan_decode(*cfg, num_seqs, q_start_host, kv_lens_host, causal, num_workgroups, &hp);
+  if (s != MLA_OK) return s;
+  if (hp.T == 0) return MLA_OK;
+  if (hp.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < hp.ws_bytes || !aligned16(workspace))
+      return MLA_ERR_WORKSPACE;
+  }
+  return decode_planned(cfg, hp, num_seqs, q_start, kv_lens, kv_lens_host, block_table,
+                        max_blocks_per_seq, num_pool_blocks, q_lat, kv_pool, causal, workspace,
+                        false, o_lat, dev_error, stream, &kv_scale);
 }
 
 }  // extern "C"

@@ -35,6 +35,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// fp32 -> e4m3 (OCP fp8: bias 7, 3 mantissa bits, largest finite 448, 0x7F NaN):
+// round to nearest, ties to even; finite magnitudes >= 448 saturate to 448; NaN
+// -> 0x7F.  Integer arithmetic only, so the code is the same on every device.
+__device__ __host__ __forceinline__ uint8_t f32_to_e4m3(float x) {
+  uint32_t u;
+  __builtin_memcpy(&u, &x, 4);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7f;                  // NaN
+  if (a >= 0x43e00000u) return (uint8_t)(sign | 0x7eu);  // >= 448 (and inf)
+  if (a < 0x3c800000u) {                             // below 2^-6: quantum 2^-9
+    // a * 2^9 < 8 is exact in fp32; round it to an integer, ties to even
+    float v;
+    __builtin_memcpy(&v, &a, 4);
+    v *= 512.0f;
+    const uint32_t m = (uint32_t)__builtin_rintf(v);  // 0..8 (8 = smallest normal)
+    return (uint8_t)(sign | m);
+  }
+  // normal: keep 3 of the 23 mantissa bits, ties to even; a carry moves into
+  // the exponent; rebias 127 -> 7
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+  uint32_t code = r - (120u << 3);
+  if (code > 0x7eu) code = 0x7eu;
+  return (uint8_t)(sign | code);
+}
+
 template <typename T> struct Storage;
 template <> struct Storage<float> {
   __device__ static __forceinline__ float load(const float* p) { return *p; }
@@ -142,6 +168,12 @@ struct DecodeArgs {
 };
 hipError_t launch_decode_generic(const mla_config& c, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_v3(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_fp8(const DecodeArgs& a, float kv_scale, hipStream_t st);
+hipError_t launch_append_fp8(int T, const void* c_kv, const void* k_pe, const void* q_pe,
+                             const int32_t* seq, const int32_t* pos, const int32_t* bt,
+                             int num_seqs, int max_blocks, int64_t num_blocks, const float* cos,
+                             const float* sin, int max_pos, float inv_scale, void* pool,
+                             void* q_lat, uint32_t* err, hipStream_t st);
 hipError_t launch_merge(const mla_config& c, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_merge_v3(const DecodeArgs& a, hipStream_t st);
 

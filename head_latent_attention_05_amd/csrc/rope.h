@@ -22,29 +22,36 @@ __device__ __forceinline__ void rope_pair(float x1, float x2, float c, float s, 
   y2 = d + e;
 }
 
-// DeepSeek-V3 RoPE width (64, 32 pairs), bf16: rotates the 8 pairs i0 .. i0+7
-// of x (16-byte loads and stores; x and y 16-byte aligned).
-__device__ __forceinline__ void rope8_bf16(const uint16_t* x, const float* cr, const float* sr,
-                                           int i0, uint16_t* y) {
+// DeepSeek-V3 RoPE width (64, 32 pairs), bf16 input: rotates the 8 pairs
+// i0 .. i0+7 of x into fp32 y1[j] (element i0+j) and y2[j] (element i0+32+j)
+// (16-byte loads; x 16-byte aligned).
+__device__ __forceinline__ void rope8_pairs(const uint16_t* x, const float* cr, const float* sr,
+                                            int i0, float* y1, float* y2) {
   const u32x4 a = *(const u32x4*)(x + i0);            // x[i0 .. i0+7]
   const u32x4 b = *(const u32x4*)(x + kV3Half + i0);  // x[i0+32 .. i0+39]
   const f32x4 c0 = *(const f32x4*)(cr + i0), c1 = *(const f32x4*)(cr + i0 + 4);
   const f32x4 s0 = *(const f32x4*)(sr + i0), s1 = *(const f32x4*)(sr + i0 + 4);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float x1 = bf16_bits_to_f32((uint16_t)(a[j >> 1] >> (16 * (j & 1))));
+    const float x2 = bf16_bits_to_f32((uint16_t)(b[j >> 1] >> (16 * (j & 1))));
+    const float c = j < 4 ? c0[j] : c1[j - 4];
+    const float sn = j < 4 ? s0[j] : s1[j - 4];
+    rope_pair(x1, x2, c, sn, y1[j], y2[j]);
+  }
+}
+
+// The same rotation stored as bf16 (nearest even) at y + i0 and y + 32 + i0
+// (16-byte stores; y 16-byte aligned).
+__device__ __forceinline__ void rope8_bf16(const uint16_t* x, const float* cr, const float* sr,
+                                           int i0, uint16_t* y) {
+  float y1[8], y2[8];
+  rope8_pairs(x, cr, sr, i0, y1, y2);
   uint32_t o1[4], o2[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    float y1[2], y2[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int j = 2 * k + e;  // pair i0 + j
-      const float x1 = bf16_bits_to_f32((uint16_t)(a[k] >> (16 * e)));
-      const float x2 = bf16_bits_to_f32((uint16_t)(b[k] >> (16 * e)));
-      const float c = j < 4 ? c0[j] : c1[j - 4];
-      const float sn = j < 4 ? s0[j] : s1[j - 4];
-      rope_pair(x1, x2, c, sn, y1[e], y2[e]);
-    }
-    o1[k] = (uint32_t)f32_to_bf16_bits(y1[0]) | ((uint32_t)f32_to_bf16_bits(y1[1]) << 16);
-    o2[k] = (uint32_t)f32_to_bf16_bits(y2[0]) | ((uint32_t)f32_to_bf16_bits(y2[1]) << 16);
+    o1[k] = (uint32_t)f32_to_bf16_bits(y1[2 * k]) | ((uint32_t)f32_to_bf16_bits(y1[2 * k + 1]) << 16);
+    o2[k] = (uint32_t)f32_to_bf16_bits(y2[2 * k]) | ((uint32_t)f32_to_bf16_bits(y2[2 * k + 1]) << 16);
   }
   *(u32x4*)(y + i0) = u32x4{o1[0], o1[1], o1[2], o1[3]};
   *(u32x4*)(y + kV3Half + i0) = u32x4{o2[0], o2[1], o2[2], o2[3]};

@@ -5,6 +5,9 @@ latent cache with the history tokens, and ``run()`` enqueues the four library
 calls of the step:
 
     mla_absorb_q -> mla_append_cache (new tokens, with q_pe) -> mla_decode -> mla_out_proj
+
+With ``kv_scale`` set the cache is e4m3 (576 bytes per token) under that
+power-of-two scale, and the append and decode calls are their fp8 forms.
 """
 from __future__ import annotations
 
@@ -18,6 +21,7 @@ from .synth import BLOCK_SIZE, Inputs
 
 SENTINEL_BF16 = 0x7FC1
 SENTINEL_F32 = 0x7FC00001
+SENTINEL_FP8 = 0x7F
 
 
 def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
@@ -37,8 +41,10 @@ def to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
 
 class DeviceStep:
     def __init__(self, inp: Inputs, device: str = "cuda:0", num_workgroups: int = 0,
-                 pool_copies: int = 1, history_chunk: int = 32768):
+                 pool_copies: int = 1, history_chunk: int = 32768,
+                 kv_scale: Optional[float] = None):
         self.inp = inp
+        self.kv_scale = kv_scale
         self.d = d = inp.dims
         self.dev = torch.device(device)
         self.cfg = B.MlaConfig.from_dims(d, BLOCK_SIZE)
@@ -83,6 +89,8 @@ class DeviceStep:
 
     def _new_pool(self, rows: int) -> torch.Tensor:
         d = self.d
+        if self.kv_scale:
+            return torch.full((rows, d.row), SENTINEL_FP8, dtype=torch.uint8, device=self.dev)
         if d.dtype == "bf16":
             t = torch.full((rows, d.row), SENTINEL_BF16, dtype=torch.int16, device=self.dev)
             return t.view(torch.bfloat16)
@@ -95,6 +103,14 @@ class DeviceStep:
         n = len(seqs)
         for a in range(0, n, self.history_chunk):
             b = min(n, a + self.history_chunk)
+            if self.kv_scale:
+                B.append_cache_fp8(self.cfg, to_device(ck[a:b], self.d.dtype, self.dev),
+                                   to_device(kp[a:b], self.d.dtype, self.dev), None,
+                                   torch.from_numpy(seqs[a:b]).to(self.dev),
+                                   torch.from_numpy(pos[a:b]).to(self.dev), self.block_table,
+                                   self.num_blocks, self.rope_cos, self.rope_sin, self.kv_scale,
+                                   pool, dev_error=self.dev_error)
+                continue
             B.append_cache(self.cfg, to_device(ck[a:b], self.d.dtype, self.dev),
                            to_device(kp[a:b], self.d.dtype, self.dev), None,
                            torch.from_numpy(seqs[a:b]).to(self.dev),
@@ -108,12 +124,26 @@ class DeviceStep:
         B.absorb_q(self.cfg, self.q_nope, self.w_uk, self.q_lat)
 
     def append(self, pool: Optional[torch.Tensor] = None) -> None:
+        if self.kv_scale:
+            B.append_cache_fp8(self.cfg, self.new_ckv, self.new_kpe, self.q_pe, self.new_seq,
+                               self.new_pos, self.block_table, self.num_blocks, self.rope_cos,
+                               self.rope_sin, self.kv_scale, self.pool if pool is None else pool,
+                               self.q_lat, dev_error=self.dev_error)
+            return
         B.append_cache(self.cfg, self.new_ckv, self.new_kpe, self.q_pe, self.new_seq,
                        self.new_pos, self.block_table, self.num_blocks, self.rope_cos,
                        self.rope_sin, self.pool if pool is None else pool, self.q_lat,
                        dev_error=self.dev_error)
 
     def decode(self, pool: Optional[torch.Tensor] = None, q_lat=None, o_lat=None) -> None:
+        if self.kv_scale:
+            B.decode_fp8(self.cfg, self.q_start, self.kv_lens, self.q_start_host,
+                         self.kv_lens_host, self.block_table, self.num_blocks,
+                         self.q_lat if q_lat is None else q_lat,
+                         self.pool if pool is None else pool, self.kv_scale, self.causal,
+                         self.o_lat if o_lat is None else o_lat, workspace=self.workspace,
+                         num_workgroups=self.num_workgroups, dev_error=self.dev_error)
+            return
         B.decode(self.cfg, self.q_start, self.kv_lens, self.q_start_host, self.kv_lens_host,
                  self.block_table, self.num_blocks, self.q_lat if q_lat is None else q_lat,
                  self.pool if pool is None else pool, self.causal,

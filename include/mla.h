@@ -330,6 +330,56 @@ mla_status mla_kv_down_append(const mla_config* cfg, int32_t T, int32_t d_model,
                               size_t workspace_bytes, void* kv_pool, void* q_lat,
                               uint32_t* dev_error, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * e4m3 (fp8) latent cache ([MLA architecture] 4.2, "量化的影响": a quantised
+ * cache halves the bytes per cached token; the page cautions that the absorbed
+ * matrices are sensitive to precision).  DeepSeek-V3 bf16 configuration only
+ * (UNSUPPORTED otherwise): the cache holds 576 bytes per token, every other
+ * tensor keeps its bf16 / fp32 type.
+ *
+ * Format and scale convention: OCP e4m3 (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; subnormals down to 2^-9; largest finite 448; 0x7F and 0xFF are
+ * NaN), one scale per cache, a power of two kv_scale in [2^-60, 2^60]
+ * (INVALID_ARG otherwise):  code = e4m3(x / kv_scale),  value = kv_scale * code.
+ * Encoding rounds to nearest, ties to even, and saturates finite magnitudes at
+ * 448.  Layout: kv_pool_fp8 [num_blocks][block_size][576] bytes, 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+
+/* mla_append_cache for an e4m3 cache.  The row holds e4m3(c_kv[t] / kv_scale)
+ * and e4m3(RoPE_p(k_pe[t]) / kv_scale), where RoPE_p is computed in fp32 with
+ * the op order of mla_append_cache and rounded once (straight from fp32 to
+ * e4m3, no bf16 step): the row is bit-exact and independent of the device.
+ * q_lat's RoPE columns are written in bf16 exactly as mla_append_cache does.
+ * Other arguments, errors and device-side checks as mla_append_cache; rope_cos
+ * and rope_sin must be 16-byte aligned. */
+mla_status mla_append_cache_fp8(const mla_config* cfg, int32_t T, const void* c_kv,
+                                const void* k_pe, const void* q_pe, const int32_t* token_seq,
+                                const int32_t* positions, const int32_t* block_table,
+                                int32_t num_seqs, int32_t max_blocks_per_seq,
+                                int64_t num_pool_blocks, const float* rope_cos,
+                                const float* rope_sin, int32_t max_pos, float kv_scale,
+                                void* kv_pool_fp8, void* q_lat, uint32_t* dev_error,
+                                void* stream);
+
+/* mla_decode over an e4m3 cache: the same attention over the dequantised rows
+ * kv_scale * code, with the same split plan and workspace
+ * (mla_decode_workspace_size), o_lat in bf16.  Both products run on fp8 MFMA:
+ * each query head's 576 values are rounded to e4m3 under a power-of-two scale
+ * 2^(e-7), where 2^e <= max|q| < 2^(e+1) over the head's values, and the
+ * softmax weights (relative to a running maximum, at most 2^8) are rounded to
+ * e4m3 for the weighted sum, while their fp32 values form the denominator.
+ * Accumulation and the softmax are fp32.  Results are run-to-run bitwise
+ * deterministic for a given split plan.  Arguments and errors as mla_decode,
+ * plus kv_scale. */
+mla_status mla_decode_fp8(const mla_config* cfg, int32_t num_seqs, const int32_t* q_start,
+                          const int32_t* kv_lens, const int32_t* q_start_host,
+                          const int32_t* kv_lens_host, const int32_t* block_table,
+                          int32_t max_blocks_per_seq, int64_t num_pool_blocks,
+                          const void* q_lat, const void* kv_pool_fp8, float kv_scale,
+                          int32_t causal, int32_t num_workgroups, void* workspace,
+                          size_t workspace_bytes, void* o_lat, uint32_t* dev_error,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

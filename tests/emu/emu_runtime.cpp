@@ -7,6 +7,8 @@
 #include <sys/mman.h>
 #include <unistd.h>
 
+#include <algorithm>
+#include <cmath>
 #include <deque>
 #include <map>
 #include <random>
@@ -315,6 +317,75 @@ void op_tr16_b64(uint64_t live, LaneIO* const* io) {
     const int g = l >> 4, i = l & 15;
     uint16_t r[4];
     for (int k = 0; k < 4; ++k) r[k] = src[16 * g + 4 * k + (i >> 2)][i & 3];
+    memcpy(io[l]->out, r, 8);
+  }
+}
+
+// OCP e4m3 value of a code (NaN for 0x7F / 0xFF)
+static double e4m3_value(unsigned char c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+  return (c & 0x80) ? -v : v;
+}
+
+double e4m3_to_double(unsigned char c) { return e4m3_value(c); }
+
+// fp32 -> e4m3 by search over the codes (nearest, ties to the even code;
+// magnitudes past 448 saturate; NaN -> 0x7F)
+unsigned char f32_to_e4m3_rne(float x) {
+  if (std::isnan(x)) return 0x7f;
+  const double a = std::min(std::fabs((double)x), 448.0);
+  int best = 0;
+  double bd = 1e300;
+  for (int c = 0; c <= 0x7e; ++c) {
+    const double d = std::fabs(e4m3_value((unsigned char)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (unsigned char)(best | (std::signbit(x) ? 0x80 : 0));
+}
+
+void op_mfma_16x16x32_fp8(uint64_t live, LaneIO* const* io) {
+  if (live != ~0ull) fail("MFMA needs all 64 lanes");
+  double A[16][32], B[32][16];
+  for (int l = 0; l < kWave; ++l) {
+    const int i = l & 15, g = l >> 4;
+    unsigned char a[8], b[8];
+    memcpy(a, io[l]->in, 8);
+    memcpy(b, io[l]->in + 8, 8);
+    for (int j = 0; j < 8; ++j) {
+      A[i][8 * g + j] = e4m3_value(a[j]);
+      B[8 * g + j][i] = e4m3_value(b[j]);
+    }
+  }
+  for (int l = 0; l < kWave; ++l) {
+    const int n = l & 15, g = l >> 4;
+    float c[4], d[4];
+    memcpy(c, io[l]->in + 16, 16);
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * g + r;
+      double s = 0;
+      for (int k = 0; k < 32; ++k) s += A[m][k] * B[k][n];
+      d[r] = (float)((double)c[r] + s);
+    }
+    memcpy(io[l]->out, d, 16);
+  }
+}
+
+void op_tr8_b64(uint64_t live, LaneIO* const* io) {
+  if (live != ~0ull) fail("transposing LDS read needs all 64 lanes");
+  const unsigned char* src[kWave];
+  for (int l = 0; l < kWave; ++l) {
+    memcpy(&src[l], io[l]->in, sizeof(void*));
+    if ((uintptr_t)src[l] & 7) fail("transposing LDS read: address not 8-byte aligned");
+  }
+  for (int l = 0; l < kWave; ++l) {
+    const int g = l >> 4, i = l & 15;
+    unsigned char r[8];
+    for (int k = 0; k < 8; ++k) r[k] = src[16 * g + 2 * k + (i >> 3)][i & 7];
     memcpy(io[l]->out, r, 8);
   }
 }

@@ -85,6 +85,23 @@ class Emu:
             p(block_table), block_table.shape[0], block_table.shape[1], num_blocks, p(cos),
             p(sin), cos.shape[0], p(pool), p(q_lat), p(dev_error), None))
 
+    def append_fp8(self, cfg, c_kv, k_pe, q_pe, seq, pos, block_table, num_blocks, cos, sin,
+                   kv_scale, pool, q_lat=None, dev_error=None) -> None:
+        p = lambda a: None if a is None else a.ctypes.data
+        self.check("mla_append_cache_fp8", self.lib.mla_append_cache_fp8(
+            ctypes.byref(cfg), c_kv.shape[0], p(c_kv), p(k_pe), p(q_pe), p(seq), p(pos),
+            p(block_table), block_table.shape[0], block_table.shape[1], num_blocks, p(cos),
+            p(sin), cos.shape[0], kv_scale, p(pool), p(q_lat), p(dev_error), None))
+
+    def decode_fp8(self, cfg, q_start, kv_lens, block_table, num_blocks, q_lat, pool, kv_scale,
+                   causal, o_lat, workspace=None, num_workgroups=0, dev_error=None) -> None:
+        p = lambda a: None if a is None else a.ctypes.data
+        ws_bytes = 0 if workspace is None else workspace.nbytes
+        self.check("mla_decode_fp8", self.lib.mla_decode_fp8(
+            ctypes.byref(cfg), len(kv_lens), p(q_start), p(kv_lens), p(q_start), p(kv_lens),
+            p(block_table), block_table.shape[1], num_blocks, p(q_lat), p(pool), kv_scale,
+            int(causal), num_workgroups, p(workspace), ws_bytes, p(o_lat), p(dev_error), None))
+
     def workspace_size(self, cfg, q_start_host, kv_lens_host, causal, num_workgroups=0) -> int:
         qs = np.ascontiguousarray(q_start_host, np.int32)
         kl = np.ascontiguousarray(kv_lens_host, np.int32)
@@ -164,10 +181,13 @@ class Emu:
 class EmuStep:
     """One decode / prefill step of a synthetic workload through the emulated
     library, mirroring the device step: history appended first (untimed set-up),
-    then absorb -> append (new tokens, with q_pe) -> decode -> out_proj."""
+    then absorb -> append (new tokens, with q_pe) -> decode -> out_proj.  With
+    ``kv_scale`` set, the cache is e4m3 under that scale (the fp8 calls)."""
 
-    def __init__(self, emu: Emu, inp: Inputs, num_workgroups: int = 0):
+    def __init__(self, emu: Emu, inp: Inputs, num_workgroups: int = 0,
+                 kv_scale: Optional[float] = None):
         self.emu, self.inp = emu, inp
+        self.kv_scale = kv_scale
         self.d = d = inp.dims
         self.cfg = B.MlaConfig.from_dims(d, BLOCK_SIZE)
         self.num_workgroups = num_workgroups
@@ -185,8 +205,10 @@ class EmuStep:
         self.cos, self.sin = emu.rope_table(max(inp.max_pos(), 1), dr)
         self.num_blocks = inp.num_blocks
         rows = inp.num_blocks * BLOCK_SIZE
-        self.pool = emu.empty((rows, d.row), st)
-        if d.dtype == "bf16":
+        self.pool = emu.empty((rows, d.row), np.uint8 if kv_scale else st)
+        if kv_scale:
+            self.pool[...] = 0x7F
+        elif d.dtype == "bf16":
             self.pool.view(np.uint16)[...] = SENTINEL_BF16
         else:
             self.pool.view(np.uint32)[...] = SENTINEL_F32
@@ -198,7 +220,11 @@ class EmuStep:
                                     num_workgroups)
         self.workspace = emu.empty((nbytes,), np.uint8) if nbytes else None
         hs, hp, hck, hkp = inp.history()
-        if len(hs):
+        if len(hs) and kv_scale:
+            emu.append_fp8(self.cfg, put(hck), put(hkp), None, put(hs.astype(np.int32)),
+                           put(hp.astype(np.int32)), self.block_table, self.num_blocks,
+                           self.cos, self.sin, kv_scale, self.pool, dev_error=self.dev_error)
+        elif len(hs):
             emu.append(self.cfg, put(hck), put(hkp), None, put(hs.astype(np.int32)),
                        put(hp.astype(np.int32)), self.block_table, self.num_blocks, self.cos,
                        self.sin, self.pool, dev_error=self.dev_error)
@@ -208,6 +234,11 @@ class EmuStep:
 
     def append(self):
         ck, kp, seq, pos = self.new
+        if self.kv_scale:
+            self.emu.append_fp8(self.cfg, ck, kp, self.q_pe, seq, pos, self.block_table,
+                                self.num_blocks, self.cos, self.sin, self.kv_scale, self.pool,
+                                self.q_lat, self.dev_error)
+            return
         self.emu.append(self.cfg, ck, kp, self.q_pe, seq, pos, self.block_table,
                         self.num_blocks, self.cos, self.sin, self.pool, self.q_lat,
                         self.dev_error)
@@ -219,6 +250,11 @@ class EmuStep:
             nbytes = self.emu.workspace_size(self.cfg, self.inp.q_start, self.inp.kv_lens,
                                              self.inp.workload.causal, nwg)
             ws = self.emu.empty((nbytes,), np.uint8) if nbytes else None
+        if self.kv_scale:
+            self.emu.decode_fp8(self.cfg, self.q_start, self.kv_lens, self.block_table,
+                                self.num_blocks, self.q_lat, self.pool, self.kv_scale,
+                                self.inp.workload.causal, self.o_lat, ws, nwg, self.dev_error)
+            return
         self.emu.decode(self.cfg, self.q_start, self.kv_lens, self.block_table,
                         self.num_blocks, self.q_lat, self.pool, self.inp.workload.causal,
                         self.o_lat, ws, nwg, self.dev_error)

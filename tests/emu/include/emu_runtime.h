@@ -22,6 +22,10 @@
 //     B[8g..8g+7][i] (8 bf16 each) and D[4g..4g+3][i] (4 fp32);
 //   ds_read_b64_tr_b16: in each 16-lane group, lane j supplies 4 consecutive
 //     16-bit values src[j][0..3]; lane i receives src[4r + i/4][i%4], r = 0..3.
+//   v_mfma_f32_16x16x32_fp8_fp8: as the bf16 form with 8 OCP e4m3 bytes per
+//     lane (A[i][8g..8g+7], B[8g..8g+7][i]);
+//   ds_read_b64_tr_b8: in each 16-lane group, lane j supplies 8 consecutive
+//     bytes src[j][0..7]; lane i receives src[2r + i/8][i%8], r = 0..7.
 #pragma once
 
 #include <math.h>
@@ -62,6 +66,9 @@ void run_grid(dim3 grid, dim3 block, const std::function<void()>& body);
 
 void op_mfma_16x16x32_bf16(uint64_t live, LaneIO* const* io);
 void op_tr16_b64(uint64_t live, LaneIO* const* io);
+void op_mfma_16x16x32_fp8(uint64_t live, LaneIO* const* io);
+void op_tr8_b64(uint64_t live, LaneIO* const* io);
+unsigned char f32_to_e4m3_rne(float x);
 void op_gather(uint64_t live, LaneIO* const* io);
 void op_ballot(uint64_t live, LaneIO* const* io);
 void op_first(uint64_t live, LaneIO* const* io);
@@ -81,6 +88,44 @@ inline f32x4_t mfma_16x16x32_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   f32x4_t d;
   wave_op(op_mfma_16x16x32_bf16, in, sizeof in, &d, sizeof d);
   return d;
+}
+
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+inline f32x4_t mfma_16x16x32_fp8(long a, long b, f32x4_t c) {
+  unsigned char in[32];
+  memcpy(in, &a, 8);
+  memcpy(in + 8, &b, 8);
+  memcpy(in + 16, &c, 16);
+  f32x4_t d;
+  wave_op(op_mfma_16x16x32_fp8, in, sizeof in, &d, sizeof d);
+  return d;
+}
+
+inline i32x2_t tr8_b64(const void* p) {
+  i32x2_t r;
+  wave_op(op_tr8_b64, &p, sizeof p, &r, sizeof r);
+  return r;
+}
+
+// v_cvt_pk_fp8_f32: a, b -> two e4m3 (nearest even) in the low (hi = false) or
+// high 16 bits of old
+inline int cvt_pk_fp8(float a, float b, int old, bool hi) {
+  const unsigned v = (unsigned)f32_to_e4m3_rne(a) | ((unsigned)f32_to_e4m3_rne(b) << 8);
+  const unsigned o = (unsigned)old;
+  return (int)(hi ? ((o & 0xffffu) | (v << 16)) : ((o & 0xffff0000u) | v));
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+double e4m3_to_double(unsigned char c);
+
+// v_cvt_pk_f32_fp8: bytes 0, 1 (hi = false) or 2, 3 of v -> two fp32 (exact)
+inline f32x2_t cvt_pk_f32_fp8(int v, bool hi) {
+  const unsigned u = (unsigned)v >> (hi ? 16 : 0);
+  f32x2_t r;
+  r[0] = (float)e4m3_to_double((unsigned char)(u & 0xff));
+  r[1] = (float)e4m3_to_double((unsigned char)((u >> 8) & 0xff));
+  return r;
 }
 
 inline i16x4_t tr16_b64(const void* p) {

@@ -126,6 +126,11 @@ inline unsigned long long __ballot(int pred) {
 #define __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, cbsz, abid, blgp) \
   ::emu::mfma_16x16x32_bf16((a), (b), (c))
 #define __builtin_amdgcn_ds_read_tr16_b64_v4i16(p) ::emu::tr16_b64((const void*)(p))
+#define __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, cbsz, abid, blgp) \
+  ::emu::mfma_16x16x32_fp8((a), (b), (c))
+#define __builtin_amdgcn_ds_read_tr8_b64_v2i32(p) ::emu::tr8_b64((const void*)(p))
+#define __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, hi) ::emu::cvt_pk_fp8((a), (b), (old), (hi))
+#define __builtin_amdgcn_cvt_pk_f32_fp8(v, hi) ::emu::cvt_pk_f32_fp8((v), (hi))
 #define __builtin_amdgcn_readfirstlane(x) ::emu::readfirstlane(x)
 #define __builtin_amdgcn_permlane16_swap(a, b, fi, bc) ::emu::permlane_swap((a), 16)
 #define __builtin_amdgcn_permlane32_swap(a, b, fi, bc) ::emu::permlane_swap((a), 32)

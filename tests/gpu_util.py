@@ -42,6 +42,21 @@ def rows_fn(pool, inp):
     return lambda b: O.gather_rows(pool, inp.dims, 64, inp.block_table, b, int(inp.kv_lens[b]))
 
 
+# e4m3 cache: one power-of-two scale per cache, chosen so the synthetic rows
+# (RMS-normalised latents, N(0,1) RoPE keys; magnitudes below about 6) use the
+# format's upper range (codes up to about 96 of 448) and rarely its subnormals.
+FP8_KV_SCALE = 2.0 ** -4
+
+
+def oracle_pool_fp8(inp, kv_scale=FP8_KV_SCALE, which="all"):
+    return O.build_pool_fp8(inp, kv_scale, 64, which=which)
+
+
+def rows_fn_fp8(pool, inp, kv_scale=FP8_KV_SCALE):
+    return lambda b: O.gather_rows_fp8(pool, inp.dims, 64, inp.block_table, b,
+                                       int(inp.kv_lens[b]), kv_scale)
+
+
 def pool_bits(pool_np, dims):
     return pool_np.view(np.uint16) if dims.dtype == "bf16" else pool_np.view(np.uint32)
 

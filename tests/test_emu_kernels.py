@@ -20,9 +20,10 @@ from head_latent_attention_05_amd import synth
 from oracle import mla_oracle as O
 from tests.emu import build_emu
 from tests.emu.emulib import Emu, EmuStep
-from tests.gpu_util import (LOGIT_PROFILES, check_kv_down_rows, check_out, drop_queries,
-                            kv_down_slots, oracle_kv_down_rows, oracle_pool, pool_bits, rows_fn,
-                            sample_heads, scale_rows)
+from tests.gpu_util import (FP8_KV_SCALE, LOGIT_PROFILES, check_kv_down_rows, check_out,
+                            drop_queries, kv_down_slots, oracle_kv_down_rows, oracle_pool,
+                            oracle_pool_fp8, pool_bits, rows_fn, rows_fn_fp8, sample_heads,
+                            scale_rows)
 
 
 @pytest.fixture(scope="module")
@@ -478,3 +479,84 @@ def test_emu_prefill_device_lengths_disagreeing_with_host_are_flagged(emu):
         p(st.pool), p(st.w_uk), p(st.w_uv), 1, p(ws), ws.nbytes, p(out), p(st.dev_error), None)
     assert rc == 0
     assert int(st.dev_error[0]) & B.DEVERR_LENGTH
+
+
+# ---------------------------------------------------------------- e4m3 cache
+FP8_CASES = ["v3_batch_ragged", "v3_prefill_small", "v3_long_segments"]
+
+
+@pytest.mark.parametrize("name", FP8_CASES)
+def test_emu_fp8_step(emu, name):
+    """The step over an e4m3 cache: the pool matches the oracle's e4m3 pool bit
+    for bit (sentinels included), q_lat's RoPE columns match the bf16 path, and
+    the output matches naive attention over the dequantised rows at the bf16
+    tolerances."""
+    inp = _inputs(**CASES[name])
+    d = inp.dims
+    st = EmuStep(emu, inp, kv_scale=FP8_KV_SCALE)
+    st.run()
+    assert int(st.dev_error[0]) == 0
+    pool = oracle_pool_fp8(inp)
+    np.testing.assert_array_equal(st.pool, pool)
+    cos, sin = O.rope_table_f32(inp.max_pos(), d.d_rope)
+    pos = inp.token_pos()
+    qpe = O.bf16_to_f64(inp.q_pe).astype(np.float32)
+    exp = O.to_bf16_bits(O.rope_cache_f32(qpe, cos[pos][:, None, :], sin[pos][:, None, :]))
+    np.testing.assert_array_equal(st.q_lat[:, :, d.d_latent:], exp)
+    heads = sorted(set(sample_heads(d.num_heads, 8) + [64]))
+    ref = O.naive_mla(d, inp.w_uk, inp.w_uv, inp.q_nope, inp.q_pe, rows_fn_fp8(pool, inp),
+                      inp.kv_lens, inp.q_start, inp.workload.causal, heads)
+    check_out(d, st.out[:, heads], ref, f"emu fp8 {name}")
+
+
+@pytest.mark.parametrize("name", ["v3_batch_ragged", "v3_prefill_small", "v3_long_segments"])
+def test_emu_fp8_decode_splits(emu, name):
+    """Every split plan against the oracle's latent decode over the dequantised
+    rows; the same plan under another interleaving gives identical bits."""
+    inp = _inputs(**CASES[name])
+    d = inp.dims
+    st = EmuStep(emu, inp, kv_scale=FP8_KV_SCALE)
+    st.append()
+    q = synth.random_latent_queries(d, inp.T, seed=5)
+    st.q_lat[...] = q
+    pool = oracle_pool_fp8(inp)
+    heads = sample_heads(d.num_heads)
+    ref = O.latent_decode(d, O.bf16_to_f64(q), rows_fn_fp8(pool, inp), inp.kv_lens,
+                          inp.q_start, inp.workload.causal, heads)
+    tol = 2.0 ** -7 * np.abs(ref).max()
+    outs = {}
+    for G in (1, 2, 7, 0, 100000):
+        st.o_lat[...] = 0
+        st.decode(G)
+        got = O.bf16_to_f64(st.o_lat)
+        assert np.all(np.isfinite(got)), G
+        err = np.abs(got[:, heads] - ref).max()
+        assert err <= tol, (G, err, tol)
+        outs[G] = st.o_lat.copy()
+    for seed in (2, 3):
+        emu.set_seed(seed)
+        st.decode(7)
+        np.testing.assert_array_equal(st.o_lat, outs[7])
+    emu.set_seed(1)
+
+
+@pytest.mark.parametrize("profile", ["rising", "sink"])
+def test_emu_fp8_decode_wide_logit_range(emu, profile):
+    """Logits far beyond the unit spread over an e4m3 cache: the softmax weights
+    reach the lazy-rescale bound 2^8 and the rescaling path runs."""
+    base = _inputs("batch64", kv_lens=[300, 97])
+    inp = scale_rows(base, LOGIT_PROFILES[profile]([int(L) for L in base.kv_lens]))
+    d = inp.dims
+    # the scaled rows must stay inside the e4m3 range under the cache scale
+    kv_scale = 2.0 ** 2 if profile == "rising" else FP8_KV_SCALE
+    st = EmuStep(emu, inp, kv_scale=kv_scale)
+    st.run()
+    pool = oracle_pool_fp8(inp, kv_scale)
+    np.testing.assert_array_equal(st.pool, pool)
+    heads = sample_heads(d.num_heads)
+    ref = O.naive_mla(d, inp.w_uk, inp.w_uv, inp.q_nope, inp.q_pe,
+                      rows_fn_fp8(pool, inp, kv_scale), inp.kv_lens, inp.q_start, False, heads)
+    err = np.abs(st.out[:, heads] - ref)
+    assert np.all(np.isfinite(st.out[:, heads]))
+    # relative to the output's size (the scaled rows make it large)
+    assert err.max() <= 2e-2 * max(1.0, np.abs(ref).max()), (err.max(), np.abs(ref).max())
