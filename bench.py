@@ -9,7 +9,8 @@ decode call (the dominant kernel) with its algorithmic bytes, timed live with
 HIP events on the library's stream, against the HBM peak and against a 1 GiB
 device copy timed in the same run; ``workloads`` gives the decode call alone on
 the other workloads; ``cpu_baseline`` times the CPU oracle on a bounded sample
-of the step's own inputs.
+of the step's own inputs; ``fp8_cache`` repeats the step and the decode calls
+with the e4m3 latent cache (576 bytes per cached token).
 
     python bench.py [--steps K] [--warmup W] [--workload batch64]
 """
@@ -29,6 +30,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode: cached-token reads/s, % of HBM & bf16 MFMA roofline (V3 shapes)"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_FP8_PEAK_TFS = 5000.0   # MI355X dense fp8 MFMA
+FP8_KV_SCALE = 2.0 ** -4     # e4m3 cache scale of the synthetic rows (magnitudes < ~6)
 COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
 
 
@@ -38,8 +41,9 @@ def log(*a):
 
 # Sources of the decode call (its kernels, their launch and split plan): the
 # committed counters stay valid while none of these changes.
-DECODE_SOURCES = ("decode_v4.hip", "merge_v3.hip", "plan_device.h", "gfx950_asm.h",
-                  "uniform_ptr.h", "mla_internal.h", "mla_api.hip")
+DECODE_SOURCES = ("decode_v4.hip", "decode_fp8.hip", "tile_walk.h", "merge_v3.hip",
+                  "plan_device.h", "gfx950_asm.h", "uniform_ptr.h", "mla_internal.h",
+                  "mla_api.hip")
 
 
 def source_hash() -> str:
@@ -165,14 +169,15 @@ def copy_bandwidth(dev, nbytes: int = 1 << 30, reps: int = 5) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def decode_bytes_flops(inp):
+def decode_bytes_flops(inp, fp8: bool = False):
     """Algorithmic bytes and flops of one decode call: every attended row read
-    once per query token, q_lat read and o_lat written once; 2 flops per
-    multiply-add over the 576-wide scores and the 512-wide values."""
+    once per query token (1 byte per value for the e4m3 cache), q_lat read and
+    o_lat written once; 2 flops per multiply-add over the 576-wide scores and
+    the 512-wide values."""
     d = inp.dims
     esz = 2 if d.dtype == "bf16" else 4
     reads = kv_reads(inp)
-    nbytes = reads * d.row * esz + inp.T * d.num_heads * (d.row + d.d_latent) * esz
+    nbytes = reads * d.row * (1 if fp8 else esz) + inp.T * d.num_heads * (d.row + d.d_latent) * esz
     flops = reads * 2 * d.num_heads * (d.row + d.d_latent)
     return reads, nbytes, flops
 
@@ -186,9 +191,10 @@ def pool_copies_for(st, min_bytes: int = 1 << 30, cap: int = 256):
     return [st.pool] + [st.pool.clone() for _ in range(n - 1)]
 
 
-def decode_only(workload: str, calls: int, warmup: int, copy_gbs: float):
+def decode_only(workload: str, calls: int, warmup: int, copy_gbs: float, kv_scale=None):
     """Decode-call time alone on another workload (same launch configuration as
-    the headline step), over rotated cache copies."""
+    the headline step), over rotated cache copies; with kv_scale, over the e4m3
+    cache (fp8 MFMA, rated against the fp8 peak)."""
     import numpy as np
     import torch
 
@@ -196,7 +202,7 @@ def decode_only(workload: str, calls: int, warmup: int, copy_gbs: float):
     from head_latent_attention_05_amd.step import DeviceStep
 
     inp = synth.make_inputs(workload)
-    st = DeviceStep(inp)
+    st = DeviceStep(inp, kv_scale=kv_scale)
     st.absorb()
     st.append()
     pools = pool_copies_for(st)
@@ -214,16 +220,18 @@ def decode_only(workload: str, calls: int, warmup: int, copy_gbs: float):
     assert int(st.dev_error.item()) == 0
     ms = [a.elapsed_time(b) for a, b in evs]
     avg = float(np.mean(ms))
-    reads, nbytes, flops = decode_bytes_flops(inp)
+    reads, nbytes, flops = decode_bytes_flops(inp, fp8=kv_scale is not None)
     gbs = nbytes / (avg * 1e-3) / 1e9
     tfs = flops / (avg * 1e-3) / 1e12
+    peak_tfs = MFMA_FP8_PEAK_TFS if kv_scale is not None else MFMA_BF16_PEAK_TFS
     rec = {"decode_us": avg * 1e3, "p50_us": float(np.median(ms)) * 1e3, "calls": calls,
            "kv_reads": reads, "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
            "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "copy_frac": gbs / copy_gbs,
-           "mfma_tfs": tfs, "mfma_frac": tfs / MFMA_BF16_PEAK_TFS,
+           "mfma_tfs": tfs, "mfma_frac": tfs / peak_tfs, "mfma_peak_tfs": peak_tfs,
            "bound": "mfma" if inp.workload.causal and inp.T > len(inp.kv_lens) else "hbm",
            "cache_copies_rotated": len(pools)}
-    if inp.workload.causal and inp.T > len(inp.kv_lens) and inp.dims.dtype == "bf16":
+    if (inp.workload.causal and inp.T > len(inp.kv_lens) and inp.dims.dtype == "bf16"
+            and kv_scale is None):
         rec["decompressed"] = decompressed_only(st, inp, pools, calls, reads)
     del st, pools
     torch.cuda.empty_cache()
@@ -418,10 +426,10 @@ def read_counter_runs(dirs):
     return vals
 
 
-DECODE_KERNELS = ("decode_v4_kernel", "merge_v3_kernel")
+DECODE_KERNELS = ("decode_v4_kernel", "decode_fp8_kernel", "merge_v3_kernel")
 
 
-def counters_json(workload: str, dirs, out: str) -> int:
+def counters_json(workload: str, dirs, out: str, fp8: bool = False) -> int:
     """From --pmc runs of `bench.py --profile-decode N` (FETCH_SIZE and
     WRITE_SIZE each in its own run): the 1 GiB copy's counters give KiB -> byte
     factors; the decode call's HBM bytes per launch are its kernels' scaled
@@ -441,21 +449,71 @@ def counters_json(workload: str, dirs, out: str) -> int:
         if fv and wv:
             per[k] = {"fetch_bytes": sum(fv) / len(fv) * 1024 * ff,
                       "write_bytes": sum(wv) / len(wv) * 1024 * wf, "dispatches": len(fv)}
-    if "decode_v4_kernel" not in per:
+    if "decode_v4_kernel" not in per and "decode_fp8_kernel" not in per:
         log("no decode kernel counters found")
         return 1
     from head_latent_attention_05_amd import synth
-    _, alg, _ = decode_bytes_flops(synth.make_inputs(workload))
+    _, alg, _ = decode_bytes_flops(synth.make_inputs(workload), fp8=fp8)
     traffic = sum(v["fetch_bytes"] + v["write_bytes"] for v in per.values())
     rec = json.load(open(out)) if os.path.exists(out) else {}
-    rec[workload] = {"source_sha": source_hash(), "traffic_bytes": traffic,
+    key = workload + ("_fp8" if fp8 else "")
+    rec[key] = {"source_sha": source_hash(), "traffic_bytes": traffic,
                      "algorithmic_bytes": alg, "traffic_over_algorithmic": traffic / alg,
                      "fetch_factor": ff, "write_factor": wf, "kernels": per}
     with open(out, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
-    print(json.dumps(rec[workload], indent=1))
+    print(json.dumps(rec[key], indent=1))
     return 0
+
+
+def fp8_section(inp, args, copy_gbs: float, workloads) -> dict:
+    """The step of the headline workload with the e4m3 cache (absorb ->
+    fp8 append -> fp8 decode -> out_proj, timed as the bf16 step), then the fp8
+    decode call alone on each workload."""
+    import numpy as np
+    import torch
+
+    from head_latent_attention_05_amd.step import DeviceStep
+
+    d = inp.dims
+    reads = kv_reads(inp)
+    pool_bytes = inp.num_blocks * 64 * d.row
+    copies = max(1, min(16, -(-(1 << 30) // pool_bytes)))
+    st = DeviceStep(inp, pool_copies=copies, kv_scale=FP8_KV_SCALE)
+
+    def step(i):
+        p = st.pools[i % copies]
+        st.absorb()
+        st.append(p)
+        st.decode(p)
+        st.project()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_.record()
+    for i in range(args.steps):
+        step(i)
+    b_.record()
+    torch.cuda.synchronize()
+    ms = a_.elapsed_time(b_) / args.steps
+    assert int(st.dev_error.item()) == 0
+    out = {"kv_scale": FP8_KV_SCALE, "format": "OCP e4m3, one power-of-two scale per cache",
+           "decode_traffic_bytes": traffic_from_counters(args.workload + "_fp8"),
+           "step_us": ms * 1e3, "value": reads / (ms * 1e-3), "unit": "cached-token reads/s",
+           "cache_copies_rotated": copies}
+    log(f"[bench] fp8 cache step {ms*1e3:.1f} us")
+    del st
+    torch.cuda.empty_cache()
+    out["workloads"] = {}
+    for w in workloads:
+        r = decode_only(w, args.extra_calls, 2, copy_gbs, kv_scale=FP8_KV_SCALE)
+        out["workloads"][w] = r
+        log(f"[bench]   fp8 {w}: {r['decode_us']:.1f} us, {r['hbm_frac']*100:.1f} % HBM, "
+            f"{r['mfma_frac']*100:.1f} % fp8 MFMA")
+    return out
 
 
 def main() -> int:
@@ -470,18 +528,23 @@ def main() -> int:
                     help="comma-separated workloads whose decode call is also timed alone "
                          "(reported under 'workloads'); empty for none")
     ap.add_argument("--extra-calls", type=int, default=10)
+    ap.add_argument("--fp8-workloads", default="batch64,single,long,prefill",
+                    help="workloads whose decode call is also timed over the e4m3 cache "
+                         "(reported under 'fp8_cache'); empty for none")
     ap.add_argument("--pool-copies", type=int, default=0,
                     help="cache copies rotated between steps (0: enough for >= 1 GB)")
     ap.add_argument("--profile-decode", type=int, default=0, metavar="N",
                     help="counter-run mode: one 1 GiB device copy (the reference kernel for "
                          "scaling HBM byte counters), then N decode calls over the rotated "
                          "cache copies, nothing else; prints no JSON line")
+    ap.add_argument("--fp8", action="store_true",
+                    help="with --profile-decode / --counters-json: the e4m3 cache")
     ap.add_argument("--counters-json", nargs="+", metavar="DIR",
                     help="no GPU: fold rocprofv3 --pmc output directories of the "
                          "--profile-decode mode into profiles/decode_counters.json")
     args = ap.parse_args()
     if args.counters_json:
-        return counters_json(args.workload, args.counters_json, COUNTERS)
+        return counters_json(args.workload, args.counters_json, COUNTERS, fp8=args.fp8)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (decode batches "
@@ -502,6 +565,10 @@ def main() -> int:
     copies = args.pool_copies or max(1, min(8, -(-(1 << 30) // pool_bytes)))
     log(f"[bench] workload={args.workload} T={inp.T} kv_reads={reads} pool={pool_bytes/1e6:.1f} MB "
         f"x{copies}")
+    if args.profile_decode and args.fp8:
+        copies = max(1, min(16, -(-(1 << 30) // (pool_bytes // 2))))
+        st = DeviceStep(inp, pool_copies=copies, kv_scale=FP8_KV_SCALE)
+        return profile_decode(st, copies, args.profile_decode)
     st = DeviceStep(inp, pool_copies=copies)
     pools = st.pools
     if args.profile_decode:
@@ -616,9 +683,12 @@ def main() -> int:
     for k, v in rec["upstream_calls"].items():
         log(f"[bench] {k}: {v['avg_us']:.1f} us, {v['hbm_frac']*100:.1f} % HBM")
     extras = [w for w in args.extra_workloads.split(",") if w and w != args.workload]
+    fp8_work = [w for w in args.fp8_workloads.split(",") if w]
+    del st, pools
+    torch.cuda.empty_cache()
+    if fp8_work and d.dtype == "bf16":
+        rec["fp8_cache"] = fp8_section(inp, args, copy_gbs, fp8_work)
     if extras:
-        del st, pools
-        torch.cuda.empty_cache()
         rec["workloads"] = {}
         for w in extras:
             log(f"[bench] decode call alone on '{w}' ...")
