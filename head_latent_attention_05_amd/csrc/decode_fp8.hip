@@ -31,12 +31,18 @@
 // operands) and 64 value MFMAs (V^T from LDS with the 8-bit
 // transposing read ds_read_b64_tr_b8, P^T's two terms from LDS).
 //
+// Score operands: the contraction order is free as long as K and Q follow the
+// same one, so the 576 columns are dealt to (k-step, lane group) in pairs of
+// k-steps: in steps 2v and 2v+1 the lanes of group g4 hold the 16 columns of
+// chunk 4v + g4 (bytes 0-7 in step 2v, 8-15 in step 2v+1), and one 16-byte LDS
+// read per row block serves both steps.
+//
 // LDS tile layout (18 KiB): 32 latent rows of 512 B, then 32 RoPE rows of 64 B.
-// Latent row t keeps its 16-byte chunk c at c ^ F(t), F(t) = (t & 15) ^ 8*((t >> 4) & 1):
-// the score reads (rows 0..15 or 16..31, one chunk each per half-wave) and the
-// transposing reads (rows {0..7, 16..23} or {8..15, 24..31} per half-wave) both
-// touch 16 distinct chunk positions, i.e. every LDS bank once.  RoPE row t keeps
-// chunk c at c ^ ((t >> 2) & 3).
+// Latent row t keeps its 16-byte chunk c at c ^ F(t), F(t) = (t & 15) ^ 12*((t >> 4) & 1):
+// a score read of one lane group (16 rows, one chunk each) and a transposing read of
+// any two lane groups (rows {4a..4a+3, 4b..4b+3} and the same plus 16, a ^ b = 1 or
+// 2) both touch distinct chunk positions, i.e. every LDS bank at most once.  RoPE
+// row t keeps chunk c at c ^ ((t >> 2) & 3).
 #include <math.h>
 
 #include "gfx950_asm.h"
@@ -62,7 +68,7 @@ constexpr float kRescale = 8.0f;  // lazy rescale threshold (log2 units): P <= 2
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ int F(int t) { return (t & 15) ^ (((t >> 4) & 1) << 3); }
+__device__ __forceinline__ int F(int t) { return (t & 15) ^ (((t >> 4) & 1) * 12); }
 __device__ __forceinline__ int Fr(int t) { return (t >> 2) & 3; }
 
 // This wave's direct-to-LDS loads of one tile.  Latent: loads d = w and w + 8,
@@ -88,11 +94,10 @@ __device__ __forceinline__ void issue_rows(int wave, const char* blk, int last, 
 }
 
 // Per-lane geometry (lane = 16 g4 + l16; tile buffers 1 KiB aligned):
-//   score reads, k-step kk < 16: row l16 (+16), logical chunk 2kk + g4/2, half
-//     g4 % 2 -> (lat ^ 32 (kk & 7)) + 256 (kk >> 3); rows l16 + 16 at
-//     (that ^ 128) + 8192;
-//   score reads, kk = 16 + r: RoPE row l16 (+16), logical chunk 2r + g4/2 ->
-//     rope ^ 32 r; rows l16 + 16 at + 1024;
+//   score reads, k-steps 2v, 2v+1 (v < 8): row l16, logical chunk 4v + g4 ->
+//     lat ^ 64 v; row l16 + 16 (F differs by 12) at ((that) ^ 192) + 8192;
+//   score reads, k-steps 16, 17: RoPE row l16 (+16), logical chunk g4 -> rope;
+//     rows l16 + 16 at + 1024;
 //   transposing reads of feature block 8wk + f: the 16 lanes of group g4 read
 //     rows R(g4, l16/2) = 4 g4 + l16/2 (l16 < 8) or 16 + 4 g4 + l16/2 - 4,
 //     bytes 8 (l16 % 2) of the block's chunk -> val(wk) ^ 16 f; lane l16 then
@@ -103,10 +108,10 @@ struct LaneGeom {
   __device__ __forceinline__ explicit LaneGeom(uint32_t tid)
       : lane((int)(tid & 63)), l16((int)(tid & 15)), g4((int)((tid >> 4) & 3)) {}
   __device__ __forceinline__ uint32_t lat() const {
-    return l16 * kLatBytes + (((g4 >> 1) ^ l16) << 4) + 8 * (g4 & 1);
+    return l16 * kLatBytes + ((g4 ^ l16) << 4);
   }
   __device__ __forceinline__ uint32_t rope() const {
-    return kRegionB + l16 * kRopeBytes + (((g4 >> 1) ^ Fr(l16)) << 4) + 8 * (g4 & 1);
+    return kRegionB + l16 * kRopeBytes + ((g4 ^ Fr(l16)) << 4);
   }
   __device__ __forceinline__ uint32_t val(int wk) const {
     const int r = l16 >> 1;
@@ -121,7 +126,7 @@ struct Shared {
   float alpha[2][4][16];    // rescale factor [team][head block][head % 16]
   float invl[2][4][16];     // kv_scale / softmax denominator, same layout
   int desc[kWaves][kNBuf][2];  // per wave: [tile % 4] = {flags | valid rows, token}
-  u32x2 qlo[kWaves][18][64];   // Q^T lo term of each wave's heads [wave][k-step][lane]
+  u32x4 qlo[kWaves][9][64];    // Q^T lo term of each wave's heads [wave][k-step pair][lane]
 };
 
 // four fp32 -> four e4m3 (nearest even) packed in one word, a first
@@ -184,7 +189,8 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
   int issued = 0;
   bool pending_adv = false;
 
-  i32x2 qh[18];  // Q^T (e4m3 hi term) of this lane's head: columns 32kk + 8g4 .. +7
+  i32x2 qh[18];  // Q^T (e4m3 hi term) of this lane's head, k-step kk: columns
+                 // 16 (4 (kk / 2) + g4) + 8 (kk % 2) .. +7
   float qs2 = 0.f;  // log2(e) * softmax scale * kv_scale * Q scale of this lane's head
   f32x4 acc[8][4];  // [feature block][head block]
   float m_run = -INFINITY, l_part = 0.f;
@@ -220,11 +226,11 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
   // 2^(7-e) (exact) and split into hi + lo.
   auto load_q = [&](int tok) {
     const LaneGeom lg_(opaque(threadIdx.x));
-    const uint32_t q_lane = ((64 * team + 16 * wk + lg_.l16) * kRow + 8 * lg_.g4) * 2;
+    const uint32_t q_lane = ((64 * team + 16 * wk + lg_.l16) * kRow + 16 * lg_.g4) * 2;
     const char* qb = (const char*)qlat + (int64_t)tok * (kH * kRow * 2) + q_lane;
     u32x4 raw[18];
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) raw[kk] = *(const u32x4*)(qb + 64 * kk);
+    for (int kk = 0; kk < 18; ++kk) raw[kk] = *(const u32x4*)(qb + 128 * (kk >> 1) + 16 * (kk & 1));
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     uint32_t mx = 0;  // bf16 magnitudes compare as integers
 #pragma unroll
@@ -240,16 +246,21 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
     const float up = __uint_as_float((uint32_t)(127 + 7 - e) << 23);    // 2^(7-e)
     qs2 = sl2 * kv_scale * __uint_as_float((uint32_t)(127 - 7 + e) << 23);  // * 2^(e-7)
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) {
-      float f[8];
+    for (int v = 0; v < 9; ++v) {
+      i32x2 lo[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f[2 * j] = __uint_as_float(raw[kk][j] << 16) * up;
-        f[2 * j + 1] = __uint_as_float(raw[kk][j] & 0xffff0000u) * up;
+      for (int e = 0; e < 2; ++e) {
+        const int kk = 2 * v + e;
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[2 * j] = __uint_as_float(raw[kk][j] << 16) * up;
+          f[2 * j + 1] = __uint_as_float(raw[kk][j] & 0xffff0000u) * up;
+        }
+        split_fp8x8(f, qh[kk], lo[e]);
       }
-      i32x2 lo;
-      split_fp8x8(f, qh[kk], lo);
-      sh.qlo[wave][kk][lg_.lane] = u32x2{(uint32_t)lo[0], (uint32_t)lo[1]};
+      sh.qlo[wave][v][lg_.lane] =
+          u32x4{(uint32_t)lo[0][0], (uint32_t)lo[0][1], (uint32_t)lo[1][0], (uint32_t)lo[1][1]};
     }
   };
 
@@ -263,41 +274,46 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
       l_part = 0.f;
     }
     f32x4 s0 = {}, s1 = {}, t0 = {}, t1 = {};  // rows 0..15 / 16..31 x Q hi / Q lo
-    i32x2 ka[3][3];  // K operands (two row blocks) and Q lo of k-steps kk .. kk+2
+    u32x4 ka[2][3];  // K of both row blocks and Q lo, k-step pairs v and v+1
     const uint32_t la = (uint32_t)(tb - lds0) + lgm.lat();
     const uint32_t ra = (uint32_t)(tb - lds0) + lgm.rope();
-    auto ld = [&](int kk, i32x2* dst) {
+    auto ld = [&](int v, u32x4* dst) {
       uint32_t a0, a1;
-      if (kk < 16) {
-        a0 = (la ^ (32 * (kk & 7))) + 256 * (kk >> 3);
-        a1 = (a0 ^ 128) + 16 * kLatBytes;
+      if (v < 8) {
+        a0 = la ^ (64 * v);
+        a1 = (a0 ^ 192) + 16 * kLatBytes;
       } else {
-        a0 = ra ^ (32 * (kk - 16));
-        a1 = a0 + 16 * kRopeBytes;
+        a0 = ra;
+        a1 = ra + 16 * kRopeBytes;
       }
-      dst[0] = *(const i32x2*)(lds0 + a0);
-      dst[1] = *(const i32x2*)(lds0 + a1);
-      dst[2] = __builtin_bit_cast(i32x2, sh.qlo[wave][kk][lane]);
+      dst[0] = *(const u32x4*)(lds0 + a0);
+      dst[1] = *(const u32x4*)(lds0 + a1);
+      dst[2] = sh.qlo[wave][v][lane];
+    };
+    auto half = [](const u32x4& x, int e) {
+      return __builtin_bit_cast(long, u32x2{x[2 * e], x[2 * e + 1]});
     };
     ld(0, ka[0]);
-    ld(1, ka[1]);
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) {
-      if (kk + 2 < 18) ld(kk + 2, ka[(kk + 2) % 3]);
-      const long qa = __builtin_bit_cast(long, qh[kk]);
-      const long qb = __builtin_bit_cast(long, ka[kk % 3][2]);
-      const long k0 = __builtin_bit_cast(long, ka[kk % 3][0]);
-      const long k1 = __builtin_bit_cast(long, ka[kk % 3][1]);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k0, qa, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k1, qa, s1, 0, 0, 0);
-      t0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k0, qb, t0, 0, 0, 0);
-      t1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k1, qb, t1, 0, 0, 0);
+    for (int v = 0; v < 9; ++v) {
+      if (v + 1 < 9) ld(v + 1, ka[(v + 1) & 1]);
+      const u32x4* kv = ka[v & 1];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const long qa = __builtin_bit_cast(long, qh[2 * v + e]);
+        const long qb = half(kv[2], e);
+        const long k0 = half(kv[0], e), k1 = half(kv[1], e);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k0, qa, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k1, qa, s1, 0, 0, 0);
+        t0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k0, qb, t0, 0, 0, 0);
+        t1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k1, qb, t1, 0, 0, 0);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // 6 LDS reads (k-steps 0, 1)
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads (pair 0)
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // 4 MFMAs (k-step kk)
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads (k-step kk+2)
+    for (int v = 0; v < 8; ++v) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads (pair v+1)
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // 8 MFMAs (pair v)
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
