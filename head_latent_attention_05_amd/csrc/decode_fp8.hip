@@ -7,29 +7,32 @@
 // power-of-two scale per cache, value = kv_scale * e4m3.  The method is the
 // same as the bf16 kernel's ([MLA explainer] stage 2B: score = scale *
 // q_lat . row over the 576 columns, softmax over the attended rows, o_lat =
-// sum p * c_kv), with both products on v_mfma_f32_16x16x32_fp8_fp8.  The
-// cached operand is the stored e4m3 value itself; the other operand of each
-// product is split into two e4m3 terms, x = hi + lo with hi = e4m3(x) and lo =
-// e4m3(x - hi), both multiplied against the same cache operand into one fp32
-// accumulator, which carries about as many significant bits as bf16 (a single
-// e4m3 term keeps four, and costs the attention output about ten times the
-// error of the bf16 path):
-//   - each query head's 576 values are scaled by the power of two 2^(7-e), with
-//     2^e <= max|q| < 2^(e+1) over the head (scaled magnitudes stay below 256,
-//     inside the format's 448), when its token's Q is loaded;
-//   - the softmax weights P (at most 2^8 under the lazy rescaling of the
-//     running maximum) are split for the value product, while the softmax
-//     denominator sums the fp32 weights.
+// sum p * c_kv).
+//   - Scores on v_mfma_f32_16x16x32_fp8_fp8.  The cached operand is the stored
+//     e4m3 value itself; the query is split into two e4m3 terms, q = hi + lo
+//     with hi = e4m3(q) and lo = e4m3(q - hi), both multiplied against the same
+//     cache operand and summed in fp32, which keeps about as many significant
+//     bits as bf16 (one e4m3 term keeps four, and costs the attention output
+//     about ten times the error of the bf16 path).  Each query head's 576
+//     values are first scaled by the power of two 2^(7-e), 2^e <= max|q| <
+//     2^(e+1) over the head (scaled magnitudes stay below 256, inside the
+//     format's 448), when its token's Q is loaded.
+//   - Values on v_mfma_f32_16x16x32_bf16: each V^T operand (8 e4m3 values) is
+//     widened to bf16 right after its LDS read, which is exact, and the softmax
+//     weights P are bf16 as in the bf16 kernel.  A V^T operand serves four
+//     MFMAs (the team's four head blocks), so the widening costs 4 VALU
+//     instructions per 4 MFMAs; the score's K operand is read by all eight
+//     waves for only 2 MFMAs each, which is why the scores stay on fp8 MFMA.
 // The result is normalised in fp32 and rounded to bf16 (o_lat and the split
 // partials), so the merge kernel of the bf16 cache serves this kernel too.
 //
 // Structure as in the bf16 kernel: one 8-wave workgroup per KV range, all 128
 // heads; two teams of four waves in a score / value ping-pong half a tile apart;
 // 32-row tiles streamed HBM -> LDS with direct-to-LDS loads into four buffers.
-// Per tile and wave: 72 score MFMAs (K rows from LDS with 8-byte reads, Q^T's
-// hi term in 36 registers, its lo term in this wave's LDS area, read with the K
-// operands) and 64 value MFMAs (V^T from LDS with the 8-bit
-// transposing read ds_read_b64_tr_b8, P^T's two terms from LDS).
+// Per tile and wave: 72 fp8 score MFMAs (K rows from LDS, Q^T's hi term in 36
+// registers, its lo term in this wave's LDS area, read with the K operands) and
+// 32 bf16 value MFMAs (V^T from LDS with the 8-bit transposing read
+// ds_read_b64_tr_b8, P^T from LDS).
 //
 // Score operands: the contraction order is free as long as K and Q follow the
 // same one, so the 576 columns are dealt to (k-step, lane group) in pairs of
@@ -122,7 +125,7 @@ struct LaneGeom {
 
 struct Shared {
   char tiles[kNBuf][kTileBytes];
-  u32x4 pbuf[2][4][64];     // P^T fragments (e4m3 hi, lo) [team][head block][lane]
+  u32x4 pbuf[2][4][64];     // P^T fragments (bf16) [team][head block][lane]
   float alpha[2][4][16];    // rescale factor [team][head block][head % 16]
   float invl[2][4][16];     // kv_scale / softmax denominator, same layout
   int desc[kWaves][kNBuf][2];  // per wave: [tile % 4] = {flags | valid rows, token}
@@ -150,6 +153,20 @@ __device__ __forceinline__ void split_fp8x8(const float* x, i32x2& hi, i32x2& lo
     r[4 * w + 3] = x[4 * w + 3] - b[1];
   }
   lo = i32x2{pk_fp8x4(r[0], r[1], r[2], r[3]), pk_fp8x4(r[4], r[5], r[6], r[7])};
+}
+
+// eight e4m3 values -> eight bf16 (exact: e4m3 values have 4 significant bits
+// and an exponent range inside bf16's, so the fp32 value's upper half is it)
+__device__ __forceinline__ bf16x8 widen_fp8x8(i32x2 v) {
+  u32x4 o;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], false);  // bytes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], true);   // bytes 2, 3
+    o[2 * w] = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
+    o[2 * w + 1] = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
+  }
+  return __builtin_bit_cast(bf16x8, o);
 }
 
 __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
@@ -347,10 +364,8 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
     }
     l_part += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
     // P^T fragment of head block wk: k slots 0..3 = tokens 4g4+r, 4..7 = 16+4g4+r
-    i32x2 ph, pl;
-    split_fp8x8(pr, ph, pl);
-    sh.pbuf[team][wk][lane] =
-        u32x4{(uint32_t)ph[0], (uint32_t)ph[1], (uint32_t)pl[0], (uint32_t)pl[1]};
+    sh.pbuf[team][wk][lane] = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                    pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
     if (g4 == 0) sh.alpha[team][wk][l16] = alpha;
     if (d & kLastOfSeg) {
       const float l_tot = head_sum(l_part);
@@ -373,13 +388,9 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
     const int lane = lgm.lane, l16 = lgm.l16, g4 = lgm.g4;
     const f32x4 al = {sh.alpha[team][0][l16], sh.alpha[team][1][l16], sh.alpha[team][2][l16],
                       sh.alpha[team][3][l16]};
-    long pbh[4], pbl[4];
+    bf16x8 pb[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const u32x4 v = sh.pbuf[team][h][lane];
-      pbh[h] = __builtin_bit_cast(long, u32x2{v[0], v[1]});
-      pbl[h] = __builtin_bit_cast(long, u32x2{v[2], v[3]});
-    }
+    for (int h = 0; h < 4; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.pbuf[team][h][lane]);
     const bool first = (d & kFirstOfSeg) != 0;
     const bool resc =
         !first && __ballot((al[0] != 1.f) | (al[1] != 1.f) | (al[2] != 1.f) | (al[3] != 1.f)) != 0;
@@ -405,20 +416,17 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
       if (f + 3 < 8) vr[(f + 3) & 3] = ldv(f + 3);
-      const long va = __builtin_bit_cast(long, vr[f & 3]);
+      const bf16x8 va = widen_fp8x8(vr[f & 3]);
 #pragma unroll
       for (int h = 0; h < 4; ++h)
-        acc[f][h] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va, pbh[h], acc[f][h], 0, 0, 0);
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-        acc[f][h] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va, pbl[h], acc[f][h], 0, 0, 0);
+        acc[f][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[h], acc[f][h], 0, 0, 0);
     }
 #pragma unroll
     for (int f = 0; f < 5; ++f) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read (block f+3)
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // 8 MFMAs (block f)
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // 4 MFMAs (block f)
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
     if (d & kLastOfSeg) {
       const f32x4 inv = {sh.invl[team][0][l16], sh.invl[team][1][l16], sh.invl[team][2][l16],
                          sh.invl[team][3][l16]};

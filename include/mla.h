@@ -363,14 +363,15 @@ mla_status mla_append_cache_fp8(const mla_config* cfg, int32_t T, const void* c_
 
 /* mla_decode over an e4m3 cache: the same attention over the dequantised rows
  * kv_scale * code, with the same split plan and workspace
- * (mla_decode_workspace_size), o_lat in bf16.  Both products run on fp8 MFMA:
- * each query head's 576 values are rounded to e4m3 under a power-of-two scale
- * 2^(e-7), where 2^e <= max|q| < 2^(e+1) over the head's values, and the
- * softmax weights (relative to a running maximum, at most 2^8) are rounded to
- * e4m3 for the weighted sum, while their fp32 values form the denominator.
- * Accumulation and the softmax are fp32.  Results are run-to-run bitwise
- * deterministic for a given split plan.  Arguments and errors as mla_decode,
- * plus kv_scale. */
+ * (mla_decode_workspace_size), o_lat in bf16.  The scores run on fp8 MFMA: each
+ * query head's 576 values are scaled by a power of two 2^(7-e), where 2^e <=
+ * max|q| < 2^(e+1) over the head's values, and split into two e4m3 terms (hi =
+ * e4m3(q), lo = e4m3(q - hi)), both multiplied against the stored codes, so the
+ * query keeps about bf16's precision.  The weighted sum of the latents runs on
+ * bf16 MFMA: the stored codes are widened to bf16 (exact) and the softmax
+ * weights are bf16, as in mla_decode.  Accumulation and the softmax are fp32.
+ * Results are run-to-run bitwise deterministic for a given split plan.
+ * Arguments and errors as mla_decode, plus kv_scale. */
 mla_status mla_decode_fp8(const mla_config* cfg, int32_t num_seqs, const int32_t* q_start,
                           const int32_t* kv_lens, const int32_t* q_start_host,
                           const int32_t* kv_lens_host, const int32_t* block_table,
