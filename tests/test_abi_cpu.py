@@ -278,3 +278,43 @@ def test_prefill_argument_checks():
     assert call(q_nope=0) == 1
     assert call(q_nope=FAKE + 4) == 1
     assert call(ws_bytes=1024) == 3
+
+
+def test_fp8_argument_checks():
+    """The e4m3-cache calls: only the DeepSeek-V3 bf16 configuration, kv_scale a
+    power of two in [2^-60, 2^60]; other checks as their bf16 forms.  All are
+    rejected on the host, before any launch."""
+    lib = B.load()
+    c = _cfg()
+    P = ctypes.c_void_p
+    qs = np.array([0, 1], np.int32)
+    kl = np.array([100], np.int32)
+
+    def append(cfg, scale, T=2):
+        return lib.mla_append_cache_fp8(ctypes.byref(cfg), T, P(FAKE), P(FAKE), None, P(FAKE),
+                                        P(FAKE), P(FAKE), 3, 4, 10, P(FAKE), P(FAKE), 64,
+                                        ctypes.c_float(scale), P(FAKE), None, None, None)
+
+    def decode(cfg, scale):
+        return lib.mla_decode_fp8(ctypes.byref(cfg), 1, P(FAKE), P(FAKE), qs.ctypes.data,
+                                  kl.ctypes.data, P(FAKE), 2, 10, P(FAKE), P(FAKE),
+                                  ctypes.c_float(scale), 0, 1, None, 0, P(FAKE), None, None)
+
+    for bad in (0.0, -1.0, 0.1, 3.0, float("inf"), float("nan"), 2.0 ** -61, 2.0 ** 61):
+        assert append(c, bad) == 1, bad
+        assert decode(c, bad) == 1, bad
+    # fp32 test mode and other shapes are not built for the e4m3 cache
+    tiny = _cfg(synth.TINY)
+    assert append(tiny, 1.0) == 2
+    assert decode(tiny, 1.0) == 2
+    # T = 0 is a no-op; a negative T is invalid
+    assert append(c, 1.0, T=0) == 0
+    assert append(c, 1.0, T=-1) == 1
+    # misaligned pool
+    assert lib.mla_append_cache_fp8(ctypes.byref(c), 2, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE),
+                                    P(FAKE), 3, 4, 10, P(FAKE), P(FAKE), 64, ctypes.c_float(1.0),
+                                    P(FAKE + 8), None, None, None) == 1
+    # a split plan that needs a workspace, without one
+    assert lib.mla_decode_fp8(ctypes.byref(c), 1, P(FAKE), P(FAKE), qs.ctypes.data,
+                              kl.ctypes.data, P(FAKE), 2, 10, P(FAKE), P(FAKE),
+                              ctypes.c_float(1.0), 0, 2, None, 0, P(FAKE), None, None) == 3

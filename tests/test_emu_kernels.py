@@ -560,3 +560,46 @@ def test_emu_fp8_decode_wide_logit_range(emu, profile):
     assert np.all(np.isfinite(st.out[:, heads]))
     # relative to the output's size (the scaled rows make it large)
     assert err.max() <= 2e-2 * max(1.0, np.abs(ref).max()), (err.max(), np.abs(ref).max())
+
+
+def test_emu_fp8_bad_entries_and_lengths_flagged(emu):
+    """The e4m3 calls skip and flag out-of-range positions, sequence ids and
+    block ids (append) and an unassigned block (decode); device lengths that
+    disagree with the host copies are flagged before any access.  Every buffer
+    ends at a guard page, so no access outside them goes unnoticed."""
+    import ctypes
+    inp = _inputs("batch64", kv_lens=[70, 129])
+    st = EmuStep(emu, inp, kv_scale=FP8_KV_SCALE)
+    before = st.pool.copy()
+    seq = emu.put(np.array([0, 5, 0], np.int32))
+    pos = emu.put(np.array([100000, 3, 127], np.int32))
+    bt = emu.put(inp.block_table.astype(np.int32))
+    bt[0, 1] = -1
+    err = emu.empty((1,), np.uint32)
+    ck = emu.put(np.zeros((3, inp.dims.d_latent), np.uint16))
+    kp = emu.put(np.zeros((3, inp.dims.d_rope), np.uint16))
+    emu.append_fp8(st.cfg, ck, kp, None, seq, pos, bt, st.num_blocks, st.cos, st.sin,
+                   FP8_KV_SCALE, st.pool, dev_error=err)
+    e = int(err[0])
+    assert e & B.DEVERR_POSITION and e & B.DEVERR_SEQ and e & B.DEVERR_BLOCK
+    np.testing.assert_array_equal(st.pool, before)
+    st.append()
+    qs = np.ascontiguousarray(inp.q_start, np.int32)
+    kl = np.ascontiguousarray(inp.kv_lens, np.int32)
+    bad = emu.put(kl + 100)
+    p = lambda a: None if a is None else a.ctypes.data
+    st.dev_error[0] = 0
+    for G in (0, 7):
+        nbytes = emu.workspace_size(st.cfg, qs, kl, False, G)
+        ws = emu.empty((max(nbytes, 16),), np.uint8)
+        rc = emu.lib.mla_decode_fp8(
+            ctypes.byref(st.cfg), len(kl), p(st.q_start), p(bad), qs.ctypes.data, kl.ctypes.data,
+            p(st.block_table), st.block_table.shape[1], st.num_blocks, p(st.q_lat), p(st.pool),
+            ctypes.c_float(FP8_KV_SCALE), 0, G, p(ws), nbytes, p(st.o_lat), p(st.dev_error),
+            None)
+        assert rc == 0
+        assert int(st.dev_error[0]) & B.DEVERR_LENGTH
+    st.dev_error[0] = 0
+    st.block_table[1, 1] = -1
+    st.decode()
+    assert int(st.dev_error[0]) & B.DEVERR_BLOCK

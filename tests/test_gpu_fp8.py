@@ -178,3 +178,50 @@ def test_fp8_fullsize_step_sampled(name):
     ref = O.naive_mla(d, inp.w_uk, inp.w_uv, inp.q_nope[toks], inp.q_pe[toks], rows, kv,
                       q_start, inp.workload.causal, HEADS)
     check_out(d, st.out.cpu().numpy()[toks][:, HEADS], ref, f"fp8 full {name} seqs={seqs}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_error_flags_bad_entries_and_lengths(fp8):
+    """Both caches: the append skips and flags out-of-range positions, sequence
+    ids and block ids; the decode flags an unassigned block (and reads only
+    inside the pool) and flags device lengths that disagree with the host
+    copies before touching anything."""
+    from head_latent_attention_05_amd import binding as B
+    announce(f"error flags fp8={fp8}")
+    inp = synth.make_inputs("batch64", kv_lens=[70, 129])
+    st = DeviceStep(inp, kv_scale=FP8_KV_SCALE if fp8 else None)
+    dev = st.dev
+    before = st.pool.clone()
+    seq = torch.tensor([0, 5, 0], dtype=torch.int32, device=dev)
+    pos = torch.tensor([100000, 3, 127], dtype=torch.int32, device=dev)
+    bt = st.block_table.clone()
+    bt[0, 1] = -1
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ck = torch.zeros((3, inp.dims.d_latent), dtype=torch.bfloat16, device=dev)
+    kp = torch.zeros((3, inp.dims.d_rope), dtype=torch.bfloat16, device=dev)
+    if fp8:
+        B.append_cache_fp8(st.cfg, ck, kp, None, seq, pos, bt, st.num_blocks, st.rope_cos,
+                           st.rope_sin, FP8_KV_SCALE, st.pool, dev_error=err)
+    else:
+        B.append_cache(st.cfg, ck, kp, None, seq, pos, bt, st.num_blocks, st.rope_cos,
+                       st.rope_sin, st.pool, dev_error=err)
+    torch.cuda.synchronize()
+    e = int(err.item())
+    assert e & B.DEVERR_POSITION and e & B.DEVERR_SEQ and e & B.DEVERR_BLOCK
+    assert torch.equal(st.pool.view(torch.uint8), before.view(torch.uint8))
+    st.append()
+    torch.cuda.synchronize()
+    # device lengths that disagree with the host plan
+    st.dev_error.zero_()
+    good = st.kv_lens
+    st.kv_lens = good + 100
+    st.decode()
+    torch.cuda.synchronize()
+    assert int(st.dev_error.item()) & B.DEVERR_LENGTH
+    st.kv_lens = good
+    # an unassigned block in the table
+    st.dev_error.zero_()
+    st.block_table[1, 1] = -1
+    st.decode()
+    torch.cuda.synchronize()
+    assert int(st.dev_error.item()) & B.DEVERR_BLOCK
