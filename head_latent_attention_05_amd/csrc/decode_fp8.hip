@@ -8,7 +8,10 @@
 // same as the bf16 kernel's ([MLA explainer] stage 2B: score = scale *
 // q_lat . row over the 576 columns, softmax over the attended rows, o_lat =
 // sum p * c_kv).
-//   - Scores on v_mfma_f32_16x16x32_fp8_fp8.  The cached operand is the stored
+//   - Scores on v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3 operands, unit
+//     scales; twice the rate per column of the 16x16x32 fp8 form) for the 512
+//     latent columns and on v_mfma_f32_16x16x32_fp8_fp8 for the 64 RoPE
+//     columns.  The cached operand is the stored
 //     e4m3 value itself; the query is split into two e4m3 terms, q = hi + lo
 //     with hi = e4m3(q) and lo = e4m3(q - hi), both multiplied against the same
 //     cache operand and summed in fp32, which keeps about as many significant
@@ -29,16 +32,17 @@
 // Structure as in the bf16 kernel: one 8-wave workgroup per KV range, all 128
 // heads; two teams of four waves in a score / value ping-pong half a tile apart;
 // 32-row tiles streamed HBM -> LDS with direct-to-LDS loads into four buffers.
-// Per tile and wave: 72 fp8 score MFMAs (K rows from LDS, Q^T's hi term in 36
-// registers, its lo term in this wave's LDS area, read with the K operands) and
-// 32 bf16 value MFMAs (V^T from LDS with the 8-bit transposing read
+// Per tile and wave: 16 fp8 score MFMAs of 128 columns and 8 of 32 (2 row
+// blocks x 2 query terms x (4 latent chunks + 2 RoPE k-steps); K rows from LDS,
+// Q^T's hi term in 36 registers, its lo term in this wave's LDS area, read with
+// the K operands) and 32 bf16 value MFMAs (V^T from LDS with the 8-bit transposing read
 // ds_read_b64_tr_b8, P^T from LDS).
 //
-// Score operands: the contraction order is free as long as K and Q follow the
-// same one, so the 576 columns are dealt to (k-step, lane group) in pairs of
-// k-steps: in steps 2v and 2v+1 the lanes of group g4 hold the 16 columns of
-// chunk 4v + g4 (bytes 0-7 in step 2v, 8-15 in step 2v+1), and one 16-byte LDS
-// read per row block serves both steps.
+// Score operands: in latent chunk v (128 columns) the lanes of group g4 hold the
+// 32 columns 128v + 32g4 .. +31 of their row (K) or head (Q), the same columns
+// for both operands; two 16-byte LDS reads per row block and chunk.  In the
+// two RoPE k-steps e = 0, 1 group g4 holds columns 512 + 16 g4 + 8 e .. +7, one
+// 16-byte read per row block for both steps.
 //
 // LDS tile layout (18 KiB): 32 latent rows of 512 B, then 32 RoPE rows of 64 B.
 // Latent row t keeps its 16-byte chunk c at c ^ F(t), F(t) = (t & 15) ^ 12*((t >> 4) & 1):
@@ -70,6 +74,7 @@ constexpr int kWaves = 8;
 constexpr float kRescale = 8.0f;  // lazy rescale threshold (log2 units): P <= 2^8
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int F(int t) { return (t & 15) ^ (((t >> 4) & 1) * 12); }
 __device__ __forceinline__ int Fr(int t) { return (t >> 2) & 3; }
@@ -97,10 +102,11 @@ __device__ __forceinline__ void issue_rows(int wave, const char* blk, int last, 
 }
 
 // Per-lane geometry (lane = 16 g4 + l16; tile buffers 1 KiB aligned):
-//   score reads, k-steps 2v, 2v+1 (v < 8): row l16, logical chunk 4v + g4 ->
-//     lat ^ 64 v; row l16 + 16 (F differs by 12) at ((that) ^ 192) + 8192;
-//   score reads, k-steps 16, 17: RoPE row l16 (+16), logical chunk g4 -> rope;
-//     rows l16 + 16 at + 1024;
+//   score reads, column chunk v < 4, half e: row l16, logical 16-byte chunk
+//     8v + 2g4 + e -> lat ^ 128 v ^ 16 e; row l16 + 16 (F differs by 12) at
+//     ((lat ^ 192) + 8192) ^ 128 v ^ 16 e;
+//   score reads, RoPE: RoPE row l16 (+16), logical chunk g4 -> rope; rows
+//     l16 + 16 at + 1024;
 //   transposing reads of feature block 8wk + f: the 16 lanes of group g4 read
 //     rows R(g4, l16/2) = 4 g4 + l16/2 (l16 < 8) or 16 + 4 g4 + l16/2 - 4,
 //     bytes 8 (l16 % 2) of the block's chunk -> val(wk) ^ 16 f; lane l16 then
@@ -111,7 +117,7 @@ struct LaneGeom {
   __device__ __forceinline__ explicit LaneGeom(uint32_t tid)
       : lane((int)(tid & 63)), l16((int)(tid & 15)), g4((int)((tid >> 4) & 3)) {}
   __device__ __forceinline__ uint32_t lat() const {
-    return l16 * kLatBytes + ((g4 ^ l16) << 4);
+    return l16 * kLatBytes + (((2 * g4) ^ l16) << 4);
   }
   __device__ __forceinline__ uint32_t rope() const {
     return kRegionB + l16 * kRopeBytes + ((g4 ^ Fr(l16)) << 4);
@@ -129,7 +135,8 @@ struct Shared {
   float alpha[2][4][16];    // rescale factor [team][head block][head % 16]
   float invl[2][4][16];     // kv_scale / softmax denominator, same layout
   int desc[kWaves][kNBuf][2];  // per wave: [tile % 4] = {flags | valid rows, token}
-  u32x4 qlo[kWaves][9][64];    // Q^T lo term of each wave's heads [wave][k-step pair][lane]
+  u32x4 qlo[kWaves][4][2][64];  // Q^T lo term of each wave's heads [wave][latent chunk][half][lane]
+  u32x4 qlo_r[kWaves][64];     // ... and of the two RoPE k-steps [wave][lane]
 };
 
 // four fp32 -> four e4m3 (nearest even) packed in one word, a first
@@ -206,8 +213,8 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
   int issued = 0;
   bool pending_adv = false;
 
-  i32x2 qh[18];  // Q^T (e4m3 hi term) of this lane's head, k-step kk: columns
-                 // 16 (4 (kk / 2) + g4) + 8 (kk % 2) .. +7
+  i32x8 qh[4];   // Q^T (e4m3 hi term) of this lane's head, chunk v: columns 128 v + 32 g4 ..
+  i32x2 qhr[2];  // ... and RoPE k-step e: columns 512 + 16 g4 + 8 e ..
   float qs2 = 0.f;  // log2(e) * softmax scale * kv_scale * Q scale of this lane's head
   f32x4 acc[8][4];  // [feature block][head block]
   float m_run = -INFINITY, l_part = 0.f;
@@ -243,18 +250,23 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
   // 2^(7-e) (exact) and split into hi + lo.
   auto load_q = [&](int tok) {
     const LaneGeom lg_(opaque(threadIdx.x));
-    const uint32_t q_lane = ((64 * team + 16 * wk + lg_.l16) * kRow + 16 * lg_.g4) * 2;
-    const char* qb = (const char*)qlat + (int64_t)tok * (kH * kRow * 2) + q_lane;
+    const uint32_t head = 64 * team + 16 * wk + lg_.l16;
+    const char* qb = (const char*)qlat + (int64_t)tok * (kH * kRow * 2) + head * (kRow * 2);
+    // raw[4v + j]: columns 128 v + 32 g4 + 8 j; raw[16 + e]: 512 + 16 g4 + 8 e
     u32x4 raw[18];
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) raw[kk] = *(const u32x4*)(qb + 128 * (kk >> 1) + 16 * (kk & 1));
+    for (int k = 0; k < 18; ++k) {
+      const uint32_t col =
+          k < 16 ? 128 * (k >> 2) + 32 * lg_.g4 + 8 * (k & 3) : 512 + 16 * lg_.g4 + 8 * (k - 16);
+      raw[k] = *(const u32x4*)(qb + 2 * col);
+    }
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     uint32_t mx = 0;  // bf16 magnitudes compare as integers
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk)
+    for (int k = 0; k < 18; ++k)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t v = raw[kk][j];
+        const uint32_t v = raw[k][j];
         mx = max(mx, max(v & 0x7fffu, (v >> 16) & 0x7fffu));
       }
     const float amax = head_max(__uint_as_float(mx << 16));
@@ -262,23 +274,31 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
     e = min(max(e, -119), 127);
     const float up = __uint_as_float((uint32_t)(127 + 7 - e) << 23);    // 2^(7-e)
     qs2 = sl2 * kv_scale * __uint_as_float((uint32_t)(127 - 7 + e) << 23);  // * 2^(e-7)
+    auto split8 = [&](const u32x4& r, i32x2& hi, i32x2& lo) {
+      float f[8];
 #pragma unroll
-    for (int v = 0; v < 9; ++v) {
-      i32x2 lo[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int kk = 2 * v + e;
-        float f[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f[2 * j] = __uint_as_float(raw[kk][j] << 16) * up;
-          f[2 * j + 1] = __uint_as_float(raw[kk][j] & 0xffff0000u) * up;
-        }
-        split_fp8x8(f, qh[kk], lo[e]);
+      for (int q = 0; q < 4; ++q) {
+        f[2 * q] = __uint_as_float(r[q] << 16) * up;
+        f[2 * q + 1] = __uint_as_float(r[q] & 0xffff0000u) * up;
       }
-      sh.qlo[wave][v][lg_.lane] =
+      split_fp8x8(f, hi, lo);
+    };
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      i32x2 hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) split8(raw[4 * v + j], hi[j], lo[j]);
+      qh[v] = i32x8{hi[0][0], hi[0][1], hi[1][0], hi[1][1], hi[2][0], hi[2][1], hi[3][0], hi[3][1]};
+      sh.qlo[wave][v][0][lg_.lane] =
           u32x4{(uint32_t)lo[0][0], (uint32_t)lo[0][1], (uint32_t)lo[1][0], (uint32_t)lo[1][1]};
+      sh.qlo[wave][v][1][lg_.lane] =
+          u32x4{(uint32_t)lo[2][0], (uint32_t)lo[2][1], (uint32_t)lo[3][0], (uint32_t)lo[3][1]};
     }
+    i32x2 lr[2];
+    split8(raw[16], qhr[0], lr[0]);
+    split8(raw[17], qhr[1], lr[1]);
+    sh.qlo_r[wave][lg_.lane] =
+        u32x4{(uint32_t)lr[0][0], (uint32_t)lr[0][1], (uint32_t)lr[1][0], (uint32_t)lr[1][1]};
   };
 
   // ---------------------------------------------------------------- S phase
@@ -291,48 +311,70 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(
       l_part = 0.f;
     }
     f32x4 s0 = {}, s1 = {}, t0 = {}, t1 = {};  // rows 0..15 / 16..31 x Q hi / Q lo
-    u32x4 ka[2][3];  // K of both row blocks and Q lo, k-step pairs v and v+1
     const uint32_t la = (uint32_t)(tb - lds0) + lgm.lat();
     const uint32_t ra = (uint32_t)(tb - lds0) + lgm.rope();
-    auto ld = [&](int v, u32x4* dst) {
-      uint32_t a0, a1;
-      if (v < 8) {
-        a0 = la ^ (64 * v);
-        a1 = (a0 ^ 192) + 16 * kLatBytes;
+    auto cat = [](const u32x4& x, const u32x4& y) {
+      return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3],
+                   (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+    };
+    auto rd32 = [&](uint32_t a0) {  // two 16-byte LDS reads (a0, a0 ^ 16) -> 32 bytes
+      return cat(*(const u32x4*)(lds0 + a0), *(const u32x4*)(lds0 + (a0 ^ 16)));
+    };
+    // Q lo of chunk v: two lane-contiguous 16-byte reads
+    auto ldl = [&](int v) { return cat(sh.qlo[wave][v][0][lane], sh.qlo[wave][v][1][lane]); };
+    // K operand of latent step st = 2v + b: chunk v, row block b
+    auto ldk = [&](int st) {
+      const int v = st >> 1, b = st & 1;
+      return rd32(b ? ((la ^ 192) + 16 * kLatBytes) ^ (128 * v) : la ^ (128 * v));
+    };
+    // eight latent steps (chunk, row block); the next step's K, and at even steps
+    // the next chunk's Q lo, are read one step ahead; the RoPE operands are read
+    // during the last two steps
+    i32x8 kc = ldk(0), ql = ldl(0), qn = {};
+    u32x4 kr0 = {}, kr1 = {}, qr = {};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int v = st >> 1;
+      i32x8 kn = {};
+      if (st + 1 < 8) kn = ldk(st + 1);
+      if ((st & 1) == 0 && v + 1 < 4) qn = ldl(v + 1);
+      if (st == 6) {
+        kr0 = *(const u32x4*)(lds0 + ra);
+        kr1 = *(const u32x4*)(lds0 + ra + 16 * kRopeBytes);
+        qr = sh.qlo_r[wave][lane];
+      }
+      if (st & 1) {
+        s1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc, qh[v], s1, 0, 0, 0, 127, 0, 127);
+        t1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc, ql, t1, 0, 0, 0, 127, 0, 127);
+        ql = qn;
       } else {
-        a0 = ra;
-        a1 = ra + 16 * kRopeBytes;
+        s0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc, qh[v], s0, 0, 0, 0, 127, 0, 127);
+        t0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kc, ql, t0, 0, 0, 0, 127, 0, 127);
       }
-      dst[0] = *(const u32x4*)(lds0 + a0);
-      dst[1] = *(const u32x4*)(lds0 + a1);
-      dst[2] = sh.qlo[wave][v][lane];
-    };
-    auto half = [](const u32x4& x, int e) {
-      return __builtin_bit_cast(long, u32x2{x[2 * e], x[2 * e + 1]});
-    };
-    ld(0, ka[0]);
-#pragma unroll
-    for (int v = 0; v < 9; ++v) {
-      if (v + 1 < 9) ld(v + 1, ka[(v + 1) & 1]);
-      const u32x4* kv = ka[v & 1];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const long qa = __builtin_bit_cast(long, qh[2 * v + e]);
-        const long qb = half(kv[2], e);
-        const long k0 = half(kv[0], e), k1 = half(kv[1], e);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k0, qa, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k1, qa, s1, 0, 0, 0);
-        t0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k0, qb, t0, 0, 0, 0);
-        t1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k1, qb, t1, 0, 0, 0);
-      }
+      kc = kn;
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads (pair 0)
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // 3 LDS reads (pair v+1)
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // 8 MFMAs (pair v)
+    for (int e = 0; e < 2; ++e) {
+      const long k0 = __builtin_bit_cast(long, u32x2{kr0[2 * e], kr0[2 * e + 1]});
+      const long k1 = __builtin_bit_cast(long, u32x2{kr1[2 * e], kr1[2 * e + 1]});
+      const long qa = __builtin_bit_cast(long, qhr[e]);
+      const long qb = __builtin_bit_cast(long, u32x2{qr[2 * e], qr[2 * e + 1]});
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k0, qa, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k1, qa, s1, 0, 0, 0);
+      t0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k0, qb, t0, 0, 0, 0);
+      t1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k1, qb, t1, 0, 0, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // K and Q lo of step 0
+#pragma unroll
+    for (int v = 0; v < 3; ++v) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // K of step 2v+1, Q lo of chunk v+1
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs (step 2v)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // K of step 2v+2
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs (step 2v+1)
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);  // K of step 7, RoPE K and Q lo
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs (step 6)
+    __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);  // step 7 and the RoPE steps
     __builtin_amdgcn_sched_barrier(0);
     s0 += t0;
     s1 += t1;

@@ -240,6 +240,7 @@ int lane_id() { return g_cur->lane; }
 
 void wave_op(WaveFn fn, const void* in, size_t nin, void* out, size_t nout) {
   Lane& L = *g_cur;
+  if (nin > sizeof L.io.in || nout > sizeof L.io.out) fail("wave collective operands too large");
   memcpy(L.io.in, in, nin);
   L.op = fn;
   L.st = AT_WAVE_OP;
@@ -369,6 +370,33 @@ void op_mfma_16x16x32_fp8(uint64_t live, LaneIO* const* io) {
       const int m = 4 * g + r;
       double s = 0;
       for (int k = 0; k < 32; ++k) s += A[m][k] * B[k][n];
+      d[r] = (float)((double)c[r] + s);
+    }
+    memcpy(io[l]->out, d, 16);
+  }
+}
+
+void op_mfma_16x16x128_f8(uint64_t live, LaneIO* const* io) {
+  if (live != ~0ull) fail("MFMA needs all 64 lanes");
+  static double A[16][128], B[128][16];
+  for (int l = 0; l < kWave; ++l) {
+    const int i = l & 15, g = l >> 4;
+    unsigned char a[32], b[32];
+    memcpy(a, io[l]->in, 32);
+    memcpy(b, io[l]->in + 32, 32);
+    for (int j = 0; j < 32; ++j) {
+      A[i][32 * g + j] = e4m3_value(a[j]);
+      B[32 * g + j][i] = e4m3_value(b[j]);
+    }
+  }
+  for (int l = 0; l < kWave; ++l) {
+    const int n = l & 15, g = l >> 4;
+    float c[4], d[4];
+    memcpy(c, io[l]->in + 64, 16);
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * g + r;
+      double s = 0;
+      for (int k = 0; k < 128; ++k) s += A[m][k] * B[k][n];
       d[r] = (float)((double)c[r] + s);
     }
     memcpy(io[l]->out, d, 16);

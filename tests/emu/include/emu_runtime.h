@@ -24,6 +24,9 @@
 //     16-bit values src[j][0..3]; lane i receives src[4r + i/4][i%4], r = 0..3.
 //   v_mfma_f32_16x16x32_fp8_fp8: as the bf16 form with 8 OCP e4m3 bytes per
 //     lane (A[i][8g..8g+7], B[8g..8g+7][i]);
+//   v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3 operands, unit scales): lane
+//     16g + i holds 32 bytes, A[i][32g..32g+31] and B[32g..32g+31][i] (the probe
+//     on MI355X showed the A and B column orders agree), D as above;
 //   ds_read_b64_tr_b8: in each 16-lane group, lane j supplies 8 consecutive
 //     bytes src[j][0..7]; lane i receives src[2r + i/8][i%8], r = 0..7.
 #pragma once
@@ -48,7 +51,7 @@ namespace emu {
 constexpr int kWave = 64;
 
 struct LaneIO {
-  alignas(16) unsigned char in[64];
+  alignas(16) unsigned char in[96];
   alignas(16) unsigned char out[64];
 };
 // A wave collective: io[l] is lane l's in/out block (null when lane l is not
@@ -68,6 +71,7 @@ void op_mfma_16x16x32_bf16(uint64_t live, LaneIO* const* io);
 void op_tr16_b64(uint64_t live, LaneIO* const* io);
 void op_mfma_16x16x32_fp8(uint64_t live, LaneIO* const* io);
 void op_tr8_b64(uint64_t live, LaneIO* const* io);
+void op_mfma_16x16x128_f8(uint64_t live, LaneIO* const* io);
 unsigned char f32_to_e4m3_rne(float x);
 void op_gather(uint64_t live, LaneIO* const* io);
 void op_ballot(uint64_t live, LaneIO* const* io);
@@ -99,6 +103,21 @@ inline f32x4_t mfma_16x16x32_fp8(long a, long b, f32x4_t c) {
   memcpy(in + 16, &c, 16);
   f32x4_t d;
   wave_op(op_mfma_16x16x32_fp8, in, sizeof in, &d, sizeof d);
+  return d;
+}
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+inline f32x4_t mfma_16x16x128_f8(i32x8_t a, i32x8_t b, f32x4_t c, int fmt_a, int fmt_b,
+                                 int scale_a, int scale_b) {
+  if (fmt_a != 0 || fmt_b != 0 || scale_a != 127 || scale_b != 127)
+    fail("16x16x128 f8f6f4: only e4m3 operands with unit scales are emulated");
+  unsigned char in[80];
+  memcpy(in, &a, 32);
+  memcpy(in + 32, &b, 32);
+  memcpy(in + 64, &c, 16);
+  f32x4_t d;
+  wave_op(op_mfma_16x16x128_f8, in, sizeof in, &d, sizeof d);
   return d;
 }
 

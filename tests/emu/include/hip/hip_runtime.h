@@ -129,6 +129,8 @@ inline unsigned long long __ballot(int pred) {
 #define __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, cbsz, abid, blgp) \
   ::emu::mfma_16x16x32_fp8((a), (b), (c))
 #define __builtin_amdgcn_ds_read_tr8_b64_v2i32(p) ::emu::tr8_b64((const void*)(p))
+#define __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, fa, fb, oa, sa, ob, sb) \
+  ::emu::mfma_16x16x128_f8((a), (b), (c), (fa), (fb), (sa), (sb))
 #define __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, hi) ::emu::cvt_pk_fp8((a), (b), (old), (hi))
 #define __builtin_amdgcn_cvt_pk_f32_fp8(v, hi) ::emu::cvt_pk_f32_fp8((v), (hi))
 #define __builtin_amdgcn_readfirstlane(x) ::emu::readfirstlane(x)
