@@ -23,7 +23,7 @@
 //   - Values on v_mfma_f32_16x16x32_bf16: each V^T operand (8 e4m3 values) is
 //     widened to bf16 right after its LDS read, which is exact, and the softmax
 //     weights P are bf16 as in the bf16 kernel.  A V^T operand serves four
-//     MFMAs (the team's four head blocks), so the widening costs 4 VALU
+//     MFMAs (the team's four head blocks), so the widening costs 8 VALU
 //     instructions per 4 MFMAs; the score's K operand is read by all eight
 //     waves for only 2 MFMAs each, which is why the scores stay on fp8 MFMA.
 // The result is normalised in fp32 and rounded to bf16 (o_lat and the split
@@ -35,8 +35,8 @@
 // Per tile and wave: 16 fp8 score MFMAs of 128 columns and 8 of 32 (2 row
 // blocks x 2 query terms x (4 latent chunks + 2 RoPE k-steps); K rows from LDS,
 // Q^T's hi term in 36 registers, its lo term in this wave's LDS area, read with
-// the K operands) and 32 bf16 value MFMAs (V^T from LDS with the 8-bit transposing read
-// ds_read_b64_tr_b8, P^T from LDS).
+// the K operands) and 32 bf16 value MFMAs (V^T from LDS with the 8-bit
+// transposing read ds_read_b64_tr_b8, P^T from LDS).
 //
 // Score operands: in latent chunk v (128 columns) the lanes of group g4 hold the
 // 32 columns 128v + 32g4 .. +31 of their row (K) or head (Q), the same columns
