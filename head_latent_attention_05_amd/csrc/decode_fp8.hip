@@ -23,7 +23,7 @@
 //   - Values on v_mfma_f32_16x16x32_bf16: each V^T operand (8 e4m3 values) is
 //     widened to bf16 right after its LDS read, which is exact, and the softmax
 //     weights P are bf16 as in the bf16 kernel.  A V^T operand serves four
-//     MFMAs (the team's four head blocks), so the widening costs 8 VALU
+//     MFMAs (the team's four head blocks), so the widening costs 4 VALU
 //     instructions per 4 MFMAs; the score's K operand is read by all eight
 //     waves for only 2 MFMAs each, which is why the scores stay on fp8 MFMA.
 // The result is normalised in fp32 and rounded to bf16 (o_lat and the split
@@ -163,15 +163,17 @@ __device__ __forceinline__ void split_fp8x8(const float* x, i32x2& hi, i32x2& lo
 }
 
 // eight e4m3 values -> eight bf16 (exact: e4m3 values have 4 significant bits
-// and an exponent range inside bf16's, so the fp32 value's upper half is it)
+// and an exponent range inside bf16's), two per v_cvt_scalef32_pk_bf16_fp8
+// with unit scale
 __device__ __forceinline__ bf16x8 widen_fp8x8(i32x2 v) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   u32x4 o;
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], false);  // bytes 0, 1
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], true);   // bytes 2, 3
-    o[2 * w] = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
-    o[2 * w + 1] = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[w], 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)v[w], 1.0f, true);
+    o[2 * w] = __builtin_bit_cast(uint32_t, a);      // bytes 0, 1
+    o[2 * w + 1] = __builtin_bit_cast(uint32_t, b);  // bytes 2, 3
   }
   return __builtin_bit_cast(bf16x8, o);
 }

@@ -147,6 +147,21 @@ inline f32x2_t cvt_pk_f32_fp8(int v, bool hi) {
   return r;
 }
 
+// v_cvt_scalef32_pk_bf16_fp8: bytes 0, 1 (hi = false) or 2, 3 of v -> two bf16,
+// times scale (only a unit scale is emulated; the conversion is then exact)
+inline unsigned cvt_scalef32_pk_bf16_fp8(unsigned v, float scale, bool hi) {
+  if (scale != 1.0f) fail("cvt_scalef32_pk_bf16_fp8: only a unit scale is emulated");
+  const unsigned u = v >> (hi ? 16 : 0);
+  unsigned r = 0;
+  for (int k = 0; k < 2; ++k) {
+    const float f = (float)e4m3_to_double((unsigned char)((u >> (8 * k)) & 0xff));
+    unsigned b;
+    memcpy(&b, &f, 4);
+    r |= (b >> 16) << (16 * k);
+  }
+  return r;
+}
+
 inline i16x4_t tr16_b64(const void* p) {
   i16x4_t r;
   wave_op(op_tr16_b64, &p, sizeof p, &r, sizeof r);

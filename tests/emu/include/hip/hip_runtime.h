@@ -133,6 +133,9 @@ inline unsigned long long __ballot(int pred) {
   ::emu::mfma_16x16x128_f8((a), (b), (c), (fa), (fb), (sa), (sb))
 #define __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, hi) ::emu::cvt_pk_fp8((a), (b), (old), (hi))
 #define __builtin_amdgcn_cvt_pk_f32_fp8(v, hi) ::emu::cvt_pk_f32_fp8((v), (hi))
+#define __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, s, hi) \
+  __builtin_bit_cast(__bf16 __attribute__((ext_vector_type(2))),                 \
+                     ::emu::cvt_scalef32_pk_bf16_fp8((v), (s), (hi)))
 #define __builtin_amdgcn_readfirstlane(x) ::emu::readfirstlane(x)
 #define __builtin_amdgcn_permlane16_swap(a, b, fi, bc) ::emu::permlane_swap((a), 16)
 #define __builtin_amdgcn_permlane32_swap(a, b, fi, bc) ::emu::permlane_swap((a), 32)
